@@ -1,0 +1,223 @@
+"""Python binding of libfa355 (exact tiled attention on MI355X / gfx950).
+
+Two layers, both argument marshalling only — every step of the computation
+runs in the HIP kernels of ``libfa355.so``:
+
+* ``fa_fwd``, ``fa_fwd_varlen``, ``fa_decode_splitkv``, ... mirror the C ABI
+  of ``include/fa355.h`` one to one (integers for device pointers and the
+  stream) and return the status code.
+* ``fwd``, ``fwd_varlen``, ``decode_splitkv`` take torch tensors (torch
+  provides device memory and streams), allocate outputs when none are
+  given, call the C ABI on the current stream and raise ``FaError`` on a
+  non-zero status.
+
+There is no fallback: if the shared library is missing or cannot be loaded,
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "FA_F32", "FA_F16", "FA_BF16",
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
+    "FaError", "library_path", "load",
+    "fa_fwd", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
+    "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
+    "fwd", "fwd_varlen", "decode_splitkv",
+]
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp]),
+    "fa_fwd_varlen_workspace_bytes": (_sz, [_i, _i]),
+    "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
+                           _sz, _i, _vp]),
+    "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz,
+                               _i, _vp]),
+    "fa_status_string": (ctypes.c_char_p, [_i]),
+    "fa_version": (ctypes.c_char_p, []),
+}
+
+
+class FaError(RuntimeError):
+    """A libfa355 call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: status %d (%s)" % (fn, status, fa_status_string(status)))
+
+
+def library_path() -> str:
+    return os.environ.get("FA355_LIB", os.path.join(_HERE, "libfa355.so"))
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa355.so (built by ``python -m exact_tiled_attention_11_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError("libfa355.so not found at %s; build it with "
+                              "`python -m exact_tiled_attention_11_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+# ---------------------------------------------------------------------------
+# C ABI, one to one
+# ---------------------------------------------------------------------------
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, dtype, stream) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, dtype, stream)
+
+
+def fa_fwd_varlen_workspace_bytes(nseq, total_q) -> int:
+    return load().fa_fwd_varlen_workspace_bytes(nseq, total_q)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H, D,
+                  scale, causal, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
+                                total_k, H, D, scale, causal, workspace, workspace_bytes, dtype,
+                                stream)
+
+
+def fa_decode_workspace_bytes(B, H, Nk_max, D, chunk) -> int:
+    return load().fa_decode_workspace_bytes(B, H, Nk_max, D, chunk)
+
+
+def fa_decode_splitkv(q, k_cache, v_cache, o, lse, seqlens_k, B, H, Nk_max, D, scale, chunk,
+                      workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_decode_splitkv(q, k_cache, v_cache, o, lse, seqlens_k, B, H, Nk_max, D,
+                                    scale, chunk, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def fa_version() -> str:
+    return load().fa_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch convenience layer
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise FaError("dtype", FA_ERR_UNSUPPORTED)
+    return codes[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != FA_OK:
+        raise FaError(fn, status)
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
+        out=None, lse=None, return_lse: bool = True, stream=None) -> Tuple:
+    """Fixed-length attention. q [B, Nq, H, D]; k, v [B, Nk, H, D] -> (o, lse [B, H, Nq])."""
+    import torch
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
+        raise ValueError("seqlens_k must be int32[B]")
+    st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D, float(scale),
+                int(bool(causal)), _ptr(seqlens_k), _dtype_code(q), _stream(stream))
+    _check("fa_fwd", st)
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
+               scale: Optional[float] = None, out=None, lse=None, return_lse: bool = True,
+               workspace=None, stream=None) -> Tuple:
+    """Packed varlen attention. q [total_q, H, D], k, v [total_k, H, D] -> (o, lse [H, total_q])."""
+    import torch
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    need = fa_fwd_varlen_workspace_bytes(max(nseq, 1), total_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                       _ptr(cu_seqlens_k), nseq, total_q, total_k, H, D, float(scale),
+                       int(bool(causal)), _ptr(workspace), workspace.numel(), _dtype_code(q),
+                       _stream(stream))
+    _check("fa_fwd_varlen", st)
+    return out, lse
+
+
+def decode_splitkv(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None,
+                   chunk: int = 256, out=None, lse=None, return_lse: bool = True,
+                   workspace=None, stream=None) -> Tuple:
+    """Split-KV decode. q [B, H, D]; caches [B, Nk_max, H, D] -> (o [B, H, D], lse [B, H])."""
+    import torch
+    B, H, D = q.shape
+    Nk_max = k_cache.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = fa_decode_workspace_bytes(B, H, Nk_max, D, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = fa_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                           _ptr(seqlens_k), B, H, Nk_max, D, float(scale), chunk,
+                           _ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
+    _check("fa_decode_splitkv", st)
+    return out, lse

@@ -1,0 +1,210 @@
+// libfa355 C ABI: argument validation, kernel selection and launch.
+//
+// Every check runs before the first HIP call, so invalid arguments are
+// reported identically on machines without a GPU.  The mapping of the
+// Hugging Face Flash-Attention-2 guide's error catalog (section 常见错误排查:
+// unsupported dtype, unsupported head_dim, unsupported GPU) onto status
+// codes is: dtype and head_dim -> FA_ERR_UNSUPPORTED, device -> FA_ERR_HIP.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "fa355.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not yet checked, 1 = gfx950, 2 = something else.  A benign cache:
+// racing threads compute the same answer.
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dtype_ok(fa_dtype_t d) { return d == FA_F32 || d == FA_F16 || d == FA_BF16; }
+
+size_t esize(fa_dtype_t d) { return d == FA_F32 ? 4 : 2; }
+
+// Current device must be a gfx950; checked once per device.
+fa_status_t device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FA_ERR_HIP;
+  if (dev < kMaxDevices) {
+    const int s = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (s == 1) return FA_OK;
+    if (s == 2) return FA_ERR_HIP;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+constexpr float kLog2eF = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or chunk size";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP error or no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_version(void) { return "libfa355 0.1.0 (gfx950)"; }
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Nq, int Nk, int D, float scale, int causal,
+                   const int32_t* seqlens_k, fa_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if ((causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  if (Nq == 0) return FA_OK;
+  if (!q || !o || ((!k || !v) && Nk > 0)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(seqlens_k))
+    return FA_ERR_INVALID_ARG;
+  // element offsets must fit the kernels' 64-bit address math and grid limits
+  const int rows = fa::fwd_block_rows(dtype, D);
+  const long long nqb = ((long long)Nq + rows - 1) / rows;
+  const long long grid = nqb * B * H;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)B * Nq > 0x7fffffffLL || (long long)B * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  (void)esize;
+
+  fa_status_t st = device_ok();
+  if (st != FA_OK) return st;
+
+  fa::FwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.seqlens_k = seqlens_k;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.nqb = (int)nqb;
+  a.c = scale * kLog2eF;
+  return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, false, (unsigned)grid,
+                                 (hipStream_t)stream));
+}
+
+size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
+  if (nseq < 1 || total_q < 0) return 0;
+  // the largest query block of any instance bounds the tile count from above
+  const int rows = 128;
+  return fa::varlen_sched_bytes(nseq, fa::varlen_max_tiles(nseq, total_q, rows));
+}
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                          int total_q, int total_k, int H, int D, float scale, int causal,
+                          void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                          void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  if (nseq < 1 || H < 1 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  if (total_q == 0) return FA_OK;
+  if (!q || !o || ((!k || !v) && total_k > 0)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  const int rows = fa::fwd_block_rows(dtype, D);
+  const long long max_tiles = fa::varlen_max_tiles(nseq, total_q, rows);
+  if (max_tiles * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  const size_t need = fa::varlen_sched_bytes(nseq, max_tiles);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  fa_status_t st = device_ok();
+  if (st != FA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = fa::launch_varlen_schedule(cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
+                                            rows, fa::fwd_key_tile(dtype, D), causal,
+                                            (int)max_tiles, (int32_t*)workspace, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  fa::FwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.sched = (const int32_t*)workspace;
+  a.nseq = nseq;
+  a.H = H;
+  a.total_q = total_q;
+  a.c = scale * kLog2eF;
+  return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, true, (unsigned)(max_tiles * H), s));
+}
+
+static bool chunk_ok(int chunk) { return chunk == 64 || chunk == 128 || chunk == 256 || chunk == 512; }
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nk_max, int D, int chunk) {
+  if (B < 1 || H < 1 || Nk_max < 0 || (D != 64 && D != 128) || !chunk_ok(chunk)) return 0;
+  const size_t nc = ((size_t)Nk_max + chunk - 1) / chunk;
+  const size_t recs = (size_t)B * H * (nc > 0 ? nc : 1);
+  const size_t o_bytes = (recs * D * 4 + 255) / 256 * 256;
+  const size_t ml_bytes = (recs * 2 * 4 + 255) / 256 * 256;
+  return o_bytes + ml_bytes;
+}
+
+fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              float* lse, const int32_t* seqlens_k, int B, int H, int Nk_max,
+                              int D, float scale, int chunk, void* workspace,
+                              size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128) || !chunk_ok(chunk)) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || Nk_max < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (!q || !o || !seqlens_k || ((!k_cache || !v_cache) && Nk_max > 0)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * (((long long)Nk_max + chunk - 1) / chunk + 1) > 0x7fffffffLL)
+    return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_workspace_bytes(B, H, Nk_max, D, chunk);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  fa_status_t st = device_ok();
+  if (st != FA_OK) return st;
+
+  const int nc = (Nk_max + chunk - 1) / chunk;
+  const size_t recs = (size_t)B * H * (nc > 0 ? nc : 1);
+  fa::DecodeArgs a = {};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.o = o;
+  a.lse = lse;
+  a.seqlens_k = seqlens_k;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float*)((char*)workspace + (recs * D * 4 + 255) / 256 * 256);
+  a.B = B;
+  a.H = H;
+  a.Nk_max = Nk_max;
+  a.NC = nc;
+  a.chunk = chunk;
+  a.c = scale * kLog2eF;
+  return from_hip(fa::launch_decode(a, dtype, D, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,309 @@
+// Split-KV decode kernels of libfa355: one query row per (batch, head)
+// against a padded key/value cache.
+//
+// Decode has a single query row, so the parallel work has to come from the
+// keys (the slavadubrov.com page, table row on prefill versus single-token
+// decode).  The cache of each (batch, head) is cut into chunks; each chunk
+// is summarised by its maximum m_c, its sum l_c and its unnormalised output
+// O_c, and the summaries are merged in a fixed order — the block summary and
+// pairwise merge of the CSDN primer 轻松读懂FlashAttention 上, section
+// Softmax求解重构, and the running (m, l) of the Ascend CANN explainer's
+// 原理 step 3.
+//
+// gfx950 mapping (ours):
+//  * partial kernel: one workgroup of chunk/64 waves per (batch, chunk,
+//    head) work item, taken in a grid-stride loop ordered chunk-major so
+//    that workgroups running together read the contiguous all-heads stretch
+//    of the cache.  Each wave issues every 16-byte K and V load of its 64
+//    keys up front (up to 32 KB in flight per wave) — the path is bound by
+//    HBM bandwidth, so the VALU work (dot products, exp2, P·V) is kept
+//    simple and overlapped by the loads of other waves.
+//  * combine kernel: one wave per (batch, head) merges the chunk summaries
+//    in chunk order; the result is bit-reproducible.
+
+#include <math.h>
+
+#include "fa_device.h"
+#include "launch.h"
+
+namespace fa {
+
+// Reduction of a value over the `width` lanes (8 or 16) of a lane group, via
+// DPP within rows of 16 lanes; afterwards every lane of the group holds it.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // xor 1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // xor 2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+  if constexpr (W == 16)
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
+  return x;
+}
+
+// Lanes 8 apart within a row of 16 (row rotate by 8).
+__device__ __forceinline__ float xor8_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float xor8_sum(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// Dot product of 8 elements held as 16 bytes, against q in fp32.
+__device__ __forceinline__ float dot8(const u32x4_t& k, const float* q, __bf16*) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = __builtin_fmaf(lo_bf16(k[e]), q[2 * e], s);
+    s = __builtin_fmaf(hi_bf16(k[e]), q[2 * e + 1], s);
+  }
+  return s;
+}
+__device__ __forceinline__ float dot8(const u32x4_t& k, const float* q, _Float16*) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f16x2_t h = as_f16x2(k[e]);
+    s = __builtin_fmaf((float)h[0], q[2 * e], s);
+    s = __builtin_fmaf((float)h[1], q[2 * e + 1], s);
+  }
+  return s;
+}
+__device__ __forceinline__ float dot8(const u32x4_t& k, const float* q, float*) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s = __builtin_fmaf(__uint_as_float(k[e]), q[e], s);
+  return s;
+}
+
+// o[0..EPL) += p * v (EPL elements held in 16 bytes).
+__device__ __forceinline__ void axpy(float* o, float p, const u32x4_t& v, __bf16*) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = __builtin_fmaf(p, lo_bf16(v[e]), o[2 * e]);
+    o[2 * e + 1] = __builtin_fmaf(p, hi_bf16(v[e]), o[2 * e + 1]);
+  }
+}
+__device__ __forceinline__ void axpy(float* o, float p, const u32x4_t& v, _Float16*) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f16x2_t h = as_f16x2(v[e]);
+    o[2 * e] = __builtin_fmaf(p, (float)h[0], o[2 * e]);
+    o[2 * e + 1] = __builtin_fmaf(p, (float)h[1], o[2 * e + 1]);
+  }
+}
+__device__ __forceinline__ void axpy(float* o, float p, const u32x4_t& v, float*) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(p, __uint_as_float(v[e]), o[e]);
+}
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void decode_partial_kernel(DecodeArgs a) {
+  constexpr int ES = Elem<T>::kBytes;
+  constexpr int EPL = 16 / ES;          // elements per 16-byte slice
+  constexpr int LPK = D * ES / 16;      // lanes per key row
+  constexpr int KPI = 64 / LPK;         // keys per wave-wide load
+  constexpr int NI = 64 / KPI;          // loads per lane for 64 keys
+  static_assert(LPK == 8 || LPK == 16 || LPK == 32, "unsupported row width");
+
+  __shared__ float red_m[NW];
+  __shared__ float red_l[NW];
+  __shared__ float red_o[NW][D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kk = lane / LPK;            // key slot within a wave-wide load
+  const int dd = lane % LPK;            // 16-byte slice of the row
+
+  const int items = a.NC * a.B * a.H;   // host guarantees < 2^31
+  const size_t rs = (size_t)a.H * D;    // elements between cache rows
+
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int cb = it / a.H;
+    const int h = it - cb * a.H;
+    const int c = cb / a.B;
+    const int b = cb - c * a.B;
+    const int lk = min(max(a.seqlens_k[b], 0), a.Nk_max);
+    if (c * a.chunk >= lk) continue;    // uniform over the workgroup
+
+    const int key0 = c * a.chunk + wave * 64;
+    const char* kb = (const char*)((const T*)a.kc + (size_t)b * a.Nk_max * rs + (size_t)h * D) + dd * 16;
+    const char* vb = (const char*)((const T*)a.vc + (size_t)b * a.Nk_max * rs + (size_t)h * D) + dd * 16;
+    u32x4_t kr[NI], vr[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int key = key0 + i * KPI + kk;
+      if (key < lk) {
+        kr[i] = *(const u32x4_t*)(kb + (size_t)key * rs * ES);
+        vr[i] = *(const u32x4_t*)(vb + (size_t)key * rs * ES);
+      } else {
+        kr[i] = u32x4_t{};
+        vr[i] = u32x4_t{};
+      }
+    }
+    // this lane's slice of q, in fp32
+    float qv[EPL];
+    {
+      const u32x4_t qr = *(const u32x4_t*)((const char*)((const T*)a.q + ((size_t)b * a.H + h) * D) + dd * 16);
+      if constexpr (ES == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[e] = __uint_as_float(qr[e]);
+      } else if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { qv[2 * e] = lo_bf16(qr[e]); qv[2 * e + 1] = hi_bf16(qr[e]); }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f16x2_t hv = as_f16x2(qr[e]);
+          qv[2 * e] = (float)hv[0];
+          qv[2 * e + 1] = (float)hv[1];
+        }
+      }
+    }
+    // scores in units of scale*log2(e)
+    float x[NI];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float s = group_sum<(LPK >= 16 ? 16 : 8)>(dot8(kr[i], qv, (T*)nullptr));
+      if constexpr (LPK == 32) s = quarter_sum(s);
+      x[i] = (key0 + i * KPI + kk < lk) ? s * a.c : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    // maximum over the wave's keys (lane groups 16 / 32 apart, and 8 apart for D*ES = 128)
+    if constexpr (LPK == 8) mx = xor8_max(mx);
+    if constexpr (LPK <= 16) mx = quarter_max(mx);
+    mx = half_max(mx);
+    if (lane == 0) red_m[wave] = mx;
+    __syncthreads();
+    float M = red_m[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red_m[w]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float p = fast_exp2(x[i] - Ms);
+      l += p;
+      axpy(o, p, vr[i], (T*)nullptr);
+    }
+    // sum over the key slots of the wave
+    if constexpr (LPK == 8) {
+      l = xor8_sum(l);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = xor8_sum(o[e]);
+    }
+    if constexpr (LPK <= 16) {
+      l = quarter_sum(l);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = quarter_sum(o[e]);
+    }
+    l = half_sum(l);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = half_sum(o[e]);
+    if (kk == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red_o[wave][dd * EPL + e] = o[e];
+      if (dd == 0) red_l[wave] = l;
+    }
+    __syncthreads();
+    const size_t rec = ((size_t)b * a.H + h) * a.NC + c;
+    for (int d = tid; d < D; d += NW * 64) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += red_o[w][d];
+      a.ws_o[rec * D + d] = s;
+    }
+    if (tid == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += red_l[w];
+      a.ws_ml[rec * 2 + 0] = M;
+      a.ws_ml[rec * 2 + 1] = s;
+    }
+    __syncthreads();  // LDS is reused by the next work item
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int DPL = (D + 63) / 64;  // output elements per lane
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H;
+  const int lk = min(max(a.seqlens_k[b], 0), a.Nk_max);
+  const int nck = (lk + a.chunk - 1) / a.chunk;
+  const float* ml = a.ws_ml + (size_t)bh * a.NC * 2;
+  const float* po = a.ws_o + (size_t)bh * a.NC * D;
+
+  float M = -INFINITY;
+  for (int c = lane; c < nck; c += 64) M = fmaxf(M, ml[2 * c]);
+  // wave-wide maximum (order does not matter for max)
+  M = fmaxf(M, __shfl_xor(M, 1));
+  M = fmaxf(M, __shfl_xor(M, 2));
+  M = fmaxf(M, __shfl_xor(M, 4));
+  M = fmaxf(M, __shfl_xor(M, 8));
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = fmaxf(M, __shfl_xor(M, 32));
+  const float Ms = (M == -INFINITY) ? 0.f : M;
+
+  float L = 0.f;
+  float o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+  for (int c = 0; c < nck; ++c) {  // fixed chunk order
+    const float w = fast_exp2(ml[2 * c] - Ms);
+    L = __builtin_fmaf(w, ml[2 * c + 1], L);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const int d = lane + 64 * e;
+      if (d < D) o[e] = __builtin_fmaf(w, po[(size_t)c * D + d], o[e]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  T* out = (T*)a.o + (size_t)bh * D;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const int d = lane + 64 * e;
+    if (d < D) out[d] = (T)(o[e] * inv);
+  }
+  if (lane == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+}
+
+template <typename T, int D, int NW>
+static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
+  // enough workgroups to keep every CU busy; the loop covers the rest
+  const long long items = (long long)a.NC * a.B * a.H;
+  const long long cap = 256LL * 8;
+  const unsigned grid = (unsigned)(items < cap ? items : cap);
+  if (grid > 0)
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_td(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.chunk) {
+    case 64: return launch_nw<T, D, 1>(a, stream);
+    case 128: return launch_nw<T, D, 2>(a, stream);
+    case 256: return launch_nw<T, D, 4>(a, stream);
+    default: return launch_nw<T, D, 8>(a, stream);
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, fa_dtype_t dtype, int D, hipStream_t stream) {
+  switch (dtype) {
+    case FA_BF16: return D == 64 ? launch_td<__bf16, 64>(a, stream) : launch_td<__bf16, 128>(a, stream);
+    case FA_F16: return D == 64 ? launch_td<_Float16, 64>(a, stream) : launch_td<_Float16, 128>(a, stream);
+    default: return D == 64 ? launch_td<float, 64>(a, stream) : launch_td<float, 128>(a, stream);
+  }
+}
+
+}  // namespace fa

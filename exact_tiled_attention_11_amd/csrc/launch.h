@@ -1,0 +1,73 @@
+// Host-side view of the libfa355 kernels: argument blocks and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa355.h"
+
+namespace fa {
+
+// Arguments of the prefill kernel (fixed-length and packed variants).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // may be null
+  const int32_t* seqlens_k;  // fixed-length: optional per-batch key count
+  const int32_t* cu_q;     // varlen: [nseq + 1]
+  const int32_t* cu_k;
+  const int32_t* sched;    // varlen: schedule written by the schedule kernel
+  int nseq;                // varlen: number of sequences
+  int B, H, Nq, Nk;        // fixed-length sizes
+  int nqb;                 // fixed-length: query blocks per (batch, head)
+  int total_q;             // varlen: lse row stride
+  float c;                 // scale * log2(e)
+};
+
+// Query rows per workgroup and keys per tile of the prefill kernel instance
+// chosen for (dtype, D).
+int fwd_block_rows(fa_dtype_t dtype, int D);
+int fwd_key_tile(fa_dtype_t dtype, int D);
+
+// Fixed-length grid: B * H * ceil(Nq / rows); varlen grid: H * max_tiles.
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype_t dtype, int D, bool causal, bool varlen,
+                      unsigned grid, hipStream_t stream);
+
+// Varlen schedule, written by one small kernel into the caller's workspace:
+//   sched[0]                 number of tiles T
+//   sched[2 + 4s .. 5 + 4s]  sequence s: first q row, q rows, first k row, k rows
+//                            (clamped to [0, total_q] / [0, total_k])
+//   sched[2 + 4*nseq + 2t]   tile t: sequence, query block; tiles sorted by
+//                            descending number of key tiles (longest first)
+hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int nseq,
+                                  int total_q, int total_k, int rows, int key_tile,
+                                  int causal, int max_tiles, int32_t* sched,
+                                  hipStream_t stream);
+
+// Upper bound on the number of (sequence, query block) tiles.
+inline long long varlen_max_tiles(int nseq, int total_q, int rows) {
+  return ((long long)total_q + rows - 1) / rows + nseq;
+}
+inline size_t varlen_sched_bytes(int nseq, long long max_tiles) {
+  size_t n = 2 + 4 * (size_t)nseq + 2 * (size_t)max_tiles;
+  return (n * 4 + 255) / 256 * 256;
+}
+
+struct DecodeArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  void* o;
+  float* lse;
+  const int32_t* seqlens_k;
+  float* ws_o;     // [B, H, NC, D]
+  float* ws_ml;    // [B, H, NC, 2]
+  int B, H, Nk_max, NC, chunk;
+  float c;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, fa_dtype_t dtype, int D, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,136 @@
+/*
+ * libfa355 — exact tiled attention (FlashAttention forward) for AMD MI355X (gfx950).
+ *
+ * The operation (all entry points): for every query row i of a (batch, head)
+ * or packed sequence,
+ *     O_i = sum_j P_ij V_j,   P_ij = exp(S_ij - m_i) / l_i,   S_ij = scale * <Q_i, K_j>,
+ *     m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i),  lse_i = m_i + ln l_i,
+ * over the keys j visible to row i.  This is standard attention as the Ascend
+ * CANN ops-transformer FlashAttention explainer states it (section 背景: S = QKᵀ,
+ * a row softmax, then times V) computed the way its section 原理 describes:
+ * query-row blocks against streamed key/value blocks with a running maximum m
+ * and running sum l (steps 1-4), so that S and P never reach device memory.
+ * The result is exact attention; only floating-point rounding order differs
+ * (Was FlashAttention bei Transformer-Inference verändert, opening section).
+ *
+ * Visibility: key j < Lk of the same sequence; with causal != 0 also
+ * j <= i + Lk - Lq (lower-triangular mask, bottom-right aligned when Lq != Lk;
+ * the Hugging Face Flash-Attention-2 integration guide, parameter table,
+ * is_causal row).  A row with no visible key gets O = 0 and lse = -inf.
+ *
+ * Precision: Q, K, V and O share one element type.  Scores, the running
+ * statistics and the output accumulator are float32.  For fp16/bf16 inputs
+ * the probabilities are rounded to the input type (round-to-nearest-even)
+ * before the P·V product; for fp32 inputs they stay fp32.  lse is float32,
+ * natural log, of the scaled scores.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *    aligned, densely packed in the stated layout; the library never
+ *    allocates, frees or retains them and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; results are valid once the stream reaches them.
+ *  - Validation happens before any HIP call.  Errors are returned as
+ *    fa_status_t; nothing is printed, thrown or aborted.  FA_ERR_HIP reports a
+ *    failed launch or a missing / non-gfx950 device.
+ *  - `scale` must be finite and >= 0 (FA_ERR_INVALID_ARG otherwise).
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    on every run (fixed reduction order, no floating-point atomics).
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define FA355_API __attribute__((visibility("default")))
+#else
+#define FA355_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned pointer, non-finite scale */
+  FA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, unsupported chunk size */
+  FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes figure */
+  FA_ERR_HIP = 4          /* no usable gfx950 device, or a kernel launch failed */
+} fa_status_t;
+
+/*
+ * Fixed-length attention (prefill).
+ *   q   : [B, Nq, H, D]   element type `dtype`
+ *   k, v: [B, Nk, H, D]
+ *   o   : [B, Nq, H, D]   written
+ *   lse : [B, H, Nq] float32, written; may be NULL (not written)
+ *   seqlens_k: device int32[B] or NULL.  If given, batch entry b has
+ *       Lk = min(max(seqlens_k[b], 0), Nk) real keys and rows Lk..Nk-1 of k
+ *       and v are padding that is never read into the result (key-padding mask;
+ *       the slavadubrov.com page's question of whether the mask and cache
+ *       layout are supported).  If NULL, Lk = Nk.  Lq = Nq always.
+ *   D in {64, 128}; B, H >= 1; Nq, Nk >= 0 (Nq == 0 is a no-op; Nk == 0 gives
+ *   empty rows).  scale is used as given (the Python binding defaults it to
+ *   1/sqrt(D), the guide's softmax_scale default).
+ */
+FA355_API fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                   const int32_t* seqlens_k, fa_dtype_t dtype, void* stream);
+
+/*
+ * Packed variable-length attention (the guide's flash_attn_varlen, FAQ 4).
+ *   q   : [total_q, H, D];  k, v: [total_k, H, D];  o: like q
+ *   lse : [H, total_q] float32 or NULL
+ *   cu_seqlens_q, cu_seqlens_k: device int32[nseq + 1], non-decreasing,
+ *       starting at 0; sequence s owns q rows cu_seqlens_q[s]..cu_seqlens_q[s+1]-1
+ *       and k/v rows cu_seqlens_k[s]..cu_seqlens_k[s+1]-1, and attends only to
+ *       its own keys.  cu_seqlens_q[nseq] must equal total_q.
+ *   workspace: device buffer of at least fa_fwd_varlen_workspace_bytes(nseq,
+ *       total_q) bytes, 16-byte aligned, used for the tile schedule; its
+ *       contents on entry do not matter.  Two calls in flight on different
+ *       streams need different workspaces.
+ */
+FA355_API size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q);
+FA355_API fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int nseq, int total_q, int total_k, int H, int D, float scale,
+                          int causal, void* workspace, size_t workspace_bytes,
+                          fa_dtype_t dtype, void* stream);
+
+/*
+ * Single-token decode with the key/value cache split into chunks (split-KV).
+ * One query row per batch entry attends to all of its Lk = min(max(seqlens_k[b],0),
+ * Nk_max) cached keys (no causal mask: the query is the newest position).
+ * Each chunk of `chunk` keys is summarised by (m_c, l_c, unnormalised O_c) and
+ * the chunks are merged in a fixed order, the block merge of the CSDN primer
+ * 轻松读懂FlashAttention 上, section Softmax求解重构.
+ *   q       : [B, H, D]
+ *   k_cache, v_cache: [B, Nk_max, H, D]; rows >= Lk are never read
+ *   o       : [B, H, D] written;  lse: [B, H] float32 or NULL
+ *   seqlens_k: device int32[B]
+ *   chunk   : keys per split, one of 64, 128, 256, 512
+ *   workspace: device buffer of at least fa_decode_workspace_bytes(...) bytes
+ *       holding the per-chunk partials; contents on entry do not matter.
+ * Two kernel launches on `stream`; stream order is the only synchronisation.
+ */
+FA355_API size_t fa_decode_workspace_bytes(int B, int H, int Nk_max, int D, int chunk);
+FA355_API fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                              void* o, float* lse, const int32_t* seqlens_k,
+                              int B, int H, int Nk_max, int D, float scale, int chunk,
+                              void* workspace, size_t workspace_bytes,
+                              fa_dtype_t dtype, void* stream);
+
+/* Static strings; never NULL. */
+FA355_API const char* fa_status_string(fa_status_t status);
+FA355_API const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

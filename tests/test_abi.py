@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_11_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+# a non-null, 16-byte aligned fake device address: never dereferenced, because
+# every call below fails validation before reaching the device
+P = 0x10000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FA355_API\s+[\w\s\*]+?\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert names == sorted([
+        "fa_fwd", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
+        "fa_decode_workspace_bytes", "fa_status_string", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert fa.fa_version().startswith("libfa355")
+
+
+def test_status_strings():
+    for code in range(5):
+        assert fa.fa_status_string(code)
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    # 64 batches x 32 heads x 128 chunks of (128 floats + 2 floats)
+    n = fa.fa_decode_workspace_bytes(64, 32, 32768, 128, 256)
+    recs = 64 * 32 * 128
+    assert n >= recs * 130 * 4 and n % 256 == 0
+    assert fa.fa_decode_workspace_bytes(64, 32, 32768, 96, 256) == 0
+    assert fa.fa_decode_workspace_bytes(64, 32, 32768, 128, 100) == 0
+    w = fa.fa_fwd_varlen_workspace_bytes(8, 100816)
+    assert w >= 4 * (2 + 4 * 8 + 2 * (100816 // 128 + 1 + 8))
+    assert fa.fa_fwd_varlen_workspace_bytes(0, 10) == 0
+
+
+def fwd_args(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, Nq=16, Nk=16, D=64, scale=0.125, causal=1,
+             seqlens_k=None, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "o", "lse", "B", "H", "Nq", "Nk", "D", "scale",
+                           "causal", "seqlens_k", "dtype", "stream")]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(D=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(q=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=MIS), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_OK),                      # no-op, no device needed
+])
+def test_fwd_validation(kw, code):
+    assert fa.fa_fwd(*fwd_args(**kw)) == code
+
+
+def test_varlen_validation():
+    base = dict(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, nseq=2, tq=10, tk=10, H=2, D=128, scale=0.1,
+                causal=1, ws=P, wsb=1 << 20, dtype=fa.FA_F16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                a["nseq"], a["tq"], a["tk"], a["H"], a["D"], a["scale"],
+                                a["causal"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+    assert call(D=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(nseq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(cq=None) == fa.FA_ERR_INVALID_ARG
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=8) == fa.FA_ERR_WORKSPACE
+    assert call(ws=MIS) == fa.FA_ERR_INVALID_ARG
+    assert call(tq=0) == fa.FA_OK
+
+
+def test_decode_validation():
+    base = dict(q=P, kc=P, vc=P, o=P, lse=P, sl=P, B=2, H=2, N=512, D=128, scale=0.1, chunk=256,
+                ws=P, wsb=1 << 20, dtype=fa.FA_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_decode_splitkv(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["sl"], a["B"],
+                                    a["H"], a["N"], a["D"], a["scale"], a["chunk"], a["ws"],
+                                    a["wsb"], a["dtype"], a["stream"])
+    assert call(chunk=100) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=256) == fa.FA_ERR_UNSUPPORTED
+    assert call(sl=None) == fa.FA_ERR_INVALID_ARG
+    assert call(B=0) == fa.FA_ERR_INVALID_ARG
+    assert call(wsb=100) == fa.FA_ERR_WORKSPACE
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(o=MIS) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    """With the library missing, the binding raises instead of computing anything."""
+    import importlib
+    monkeypatch.setenv("FA355_LIB", str(tmp_path / "missing.so"))
+    mod = importlib.reload(fa)
+    try:
+        with pytest.raises(ImportError):
+            mod.fa_version()
+    finally:
+        monkeypatch.delenv("FA355_LIB")
+        importlib.reload(fa)
