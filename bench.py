@@ -1,0 +1,247 @@
+"""Benchmark of the libfa355 hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the causal bf16 prefill at sequence 8192 (B4 H16 D64) through ``fa_fwd``,
+then the bf16 split-KV decode (B64 H32 D128, cache lengths U[4096, 32768],
+256-key chunks) through ``fa_decode_splitkv``.  Inputs are resident in HBM
+before the timed region starts.  Each call is bracketed by HIP events on the
+stream it is launched on (torch's current stream), so the per-kernel times
+are measured live; the wall clock over the K steps gives ms_per_step.
+
+The printed JSON line carries:
+* value     prefill throughput, algorithmic TFLOP/s (4*D per visible
+            query/key pair; masked and skipped pairs are not credited);
+* roofline  the prefill kernel against the dense bf16 MFMA peak;
+* decode    the decode call's algorithmic GB/s (real K/V rows read once,
+            plus q, o and lse) against the 8 TB/s HBM peak;
+* cpu_baseline the float64 CPU oracle timed on a bounded sample of the same
+            prefill workload (test infrastructure; reported, not a target).
+
+``traffic`` comes from committed rocprofv3 counter summaries under
+``profiles/`` and is reported only while the kernel source they were taken
+on is unchanged (a hash of the source files is stored with them).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["exact_tiled_attention_11_amd/csrc/fwd.hip",
+                  "exact_tiled_attention_11_amd/csrc/decode.hip",
+                  "exact_tiled_attention_11_amd/csrc/fa_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters(name):
+    """Per-launch HBM bytes from a committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def make_prefill(w, dev):
+    import workloads as wl
+    q, k, v = wl.prefill_inputs(w)
+    return q.to(dev), k.to(dev), v.to(dev)
+
+
+def make_decode(w, dev):
+    """Device caches filled entry by entry (only the real rows are drawn)."""
+    import torch
+    import workloads as wl
+    lens = w.lengths()
+    dt = torch.bfloat16
+    q = wl.decode_query(w).to(dev)
+    kc = torch.empty((w.B, w.Nk, w.H, w.D), dtype=dt, device=dev)
+    vc = torch.empty((w.B, w.Nk, w.H, w.D), dtype=dt, device=dev)
+    for b in range(w.B):
+        L = int(lens[b])
+        kc[b, :L].copy_(wl.decode_cache_rows(w, 1, b, L))
+        vc[b, :L].copy_(wl.decode_cache_rows(w, 2, b, L))
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    return q, kc, vc, sl
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle on whole (batch, head) slices of the prefill workload until
+    the time budget is spent; returns algorithmic TFLOP/s of the sample."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    q, k, v = wl.prefill_inputs(w)
+    q64, k64, v64 = wl.to_f64(q), wl.to_f64(k), wl.to_f64(v)
+    per_head_flops = 4.0 * w.D * (w.Nq * (w.Nq + 1) // 2 if w.causal else w.Nq * w.Nk)
+    done, t0 = 0, time.perf_counter()
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in pairs:
+        oracle.attention(q64[b:b + 1, :, h:h + 1], k64[b:b + 1, :, h:h + 1],
+                         v64[b:b + 1, :, h:h + 1], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": done * per_head_flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d (batch, head) slices of %s, %.1f s of float64 numpy (BLAS "
+                  "threads = cores; exp single-threaded)" % (done, len(pairs), w.name, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one call only (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: libfa355 has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import exact_tiled_attention_11_amd as fa
+
+    fa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp, wd = wl.CFG[3], wl.CFG[5]
+    do_p = args.only in (None, "prefill")
+    do_d = args.only in (None, "decode")
+
+    log("generating inputs")
+    if do_p:
+        q, k, v = make_prefill(wp, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((wp.B, wp.H, wp.Nq), dtype=torch.float32, device=dev)
+    if do_d:
+        dq, kc, vc, sl = make_decode(wd, dev)
+        do_ = torch.empty_like(dq)
+        dlse = torch.empty((wd.B, wd.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_decode_workspace_bytes(wd.B, wd.H, wd.Nk, wd.D, wd.chunk),
+                         dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if do_p:
+            if ev: ev[0].record()
+            fa.fwd(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
+            if ev: ev[1].record()
+        if do_d:
+            if ev: ev[2].record()
+            fa.decode_splitkv(dq, kc, vc, sl, scale=wd.scale, chunk=wd.chunk, out=do_, lse=dlse,
+                              workspace=ws)
+            if ev: ev[3].record()
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tp = [e[0].elapsed_time(e[1]) for e in evs] if do_p else []
+    td = [e[2].elapsed_time(e[3]) for e in evs] if do_d else []
+
+    out = {
+        "metric": "attention fwd TFLOP/s (prefill) & decode HBM GB/s, % of MI355X roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    cfg = {"workload": ""}
+    if do_p:
+        pm = sum(tp) / len(tp)
+        pflops = wp.flops()
+        achieved = pflops / (pm * 1e-3) / 1e12
+        traffic = counters("fa_fwd_causal_bf16_b4h16n8192d64.counters.json")
+        out["value"] = achieved
+        out["unit"] = "TFLOP/s"
+        out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": traffic, "kernel": "fwd_kernel<bf16,64,causal>",
+                           "ms_per_launch": pm, "ms_min": min(tp),
+                           "algorithmic_flops_per_launch": pflops}
+        cfg["workload"] = "prefill: %s" % wp.name
+        cfg["prefill"] = {"B": wp.B, "H": wp.H, "Nq": wp.Nq, "Nk": wp.Nk, "D": wp.D,
+                          "causal": True, "scale": wp.scale, "seed": wp.seed}
+    if do_d:
+        dm = sum(td) / len(td)
+        dbytes = wd.bytes_moved()
+        gbs = dbytes / (dm * 1e-3) / 1e9
+        traffic = counters("fa_decode_bf16_b64h32d128.counters.json")
+        out["decode"] = {"value": gbs, "unit": "GB/s", "ms_per_call": dm, "ms_min": min(td),
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                      "traffic": traffic,
+                                      "kernel": "decode_partial + decode_combine (one call)",
+                                      "algorithmic_bytes_per_call": dbytes}}
+        cfg["workload"] = (cfg["workload"] + " + " if cfg["workload"] else "") + "decode: %s" % wd.name
+        cfg["decode"] = {"B": wd.B, "H": wd.H, "D": wd.D, "Nk_max": wd.Nk, "chunk": wd.chunk,
+                         "sum_Lk": int(wd.lengths().sum()), "scale": wd.scale, "seed": wd.seed}
+        if not do_p:
+            out["value"], out["unit"] = gbs, "GB/s"
+            out["roofline"] = out["decode"]["roofline"]
+    out["config"] = cfg
+    if do_p and not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wp, args.cpu_budget)
+    order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+             "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+             "roofline", "decode", "cpu_baseline"]
+    print(json.dumps({k: out[k] for k in order if k in out}), flush=True)
+
+
+if __name__ == "__main__":
+    main()
