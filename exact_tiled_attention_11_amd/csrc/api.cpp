@@ -100,7 +100,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   a.Nq = Nq;
   a.Nk = Nk;
   a.nqb = (int)nqb;
-  a.c = scale * kLog2eF;
+  a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
   return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, false, (unsigned)grid,
                                  (hipStream_t)stream));
 }
@@ -153,7 +153,7 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   a.nseq = nseq;
   a.H = H;
   a.total_q = total_q;
-  a.c = scale * kLog2eF;
+  a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
   return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, true, (unsigned)(max_tiles * H), s));
 }
 
@@ -203,7 +203,7 @@ fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_
   a.Nk_max = Nk_max;
   a.NC = nc;
   a.chunk = chunk;
-  a.c = scale * kLog2eF;
+  a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
   return from_hip(fa::launch_decode(a, dtype, D, (hipStream_t)stream));
 }
 

@@ -10,34 +10,51 @@
 // partial result by exp(m_old - m_new) is the pairwise merge of the CSDN
 // primer 轻松读懂FlashAttention 上, section Softmax求解重构.  Fused into one
 // kernel, the N x N scores and probabilities live only in registers (the
-// primer's section 内存卡点 on kernel fusion).
+// primer's section 内存卡点 on kernel fusion); the explainer's 关键优化点
+// (on-chip buffer reuse, pipelining data movement with compute) become LDS
+// staging with several tiles in flight.
 //
 // gfx950 mapping (ours, not the pages'):
 //  * Each wave owns QB blocks of 32 query rows.  Scores are computed
 //    transposed, S^T = K Q^T, on the 32x32 MFMA: lane l then holds one query
 //    (column l%32) and 16 keys per 32-key block, so row maxima and sums are
 //    in-lane plus one exchange between the two 32-lane halves.
-//  * Q stays in VGPRs as the MFMA B operand for the whole kernel.
-//  * K and V tiles of KB*32 keys are double-buffered in LDS with an XOR
-//    swizzle over 16-byte chunks; the next tile's global loads are issued
-//    before the current tile's math.
+//  * Q stays in VGPRs as the MFMA B operand for the whole kernel; one FMA
+//    per score forms the exp2 exponent c*s - m (c = scale*log2 e), so a
+//    probability costs an FMA and a v_exp_f32.
+//  * The running maximum is raised lazily: only when a tile's maximum
+//    exceeds it by more than kTau (or on a row's first visible key) are the
+//    accumulator, the sum and the exponents rescaled; otherwise p <= 2^kTau.
+//    The result is the same softmax, since the final division uses the same
+//    offset as every exponent.
+//  * K and V tiles of KB*32 keys reach LDS through direct buffer loads
+//    (buffer_load_dwordx4 ... lds, no VGPR staging), NBUF tiles deep, with
+//    an XOR swizzle over 16-byte chunks chosen per lane on the global side.
+//    Rows past the end of the sequence are outside the buffer range and
+//    arrive as zeros.
 //  * The output is accumulated transposed too, O^T += V^T P^T: the
 //    probabilities never leave registers (they are the B operand as
 //    computed), and V^T fragments come from LDS with the gfx950
-//    transposing read ds_read_b64_tr_b16.
+//    transposing read ds_read_b64_tr_b16.  Row sums add the fp32
+//    probabilities before they are rounded for P V (the log-sum-exp needs
+//    that precision on rows with few keys).
 //  * Causal tiles wholly above the diagonal are never loaded; a wave whose
 //    rows cannot see a tile skips its math; only diagonal and tail tiles
 //    evaluate the mask.  Causal query blocks are issued longest first.
-//  * exp is taken as exp2 with scale*log2(e) folded into one FMA.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 #include "launch.h"
 
 namespace fa {
 
-template <typename T, int D, int QB, int KB, int NW>
+// Exponent headroom of the lazy maximum: probabilities stay below 2^kTau.
+constexpr float kTau = 8.0f;
+
+template <typename T, int D, int QB, int KB, int NW, int NBUF>
 struct FwdCfg {
   static constexpr int kQW = 32 * QB;          // query rows per wave
   static constexpr int kBR = NW * kQW;         // query rows per workgroup
@@ -47,32 +64,65 @@ struct FwdCfg {
   static constexpr int kRowB = D * kES;        // bytes of one K or V row
   static constexpr int kCPR = kRowB / 16;      // 16-byte chunks per row
   static constexpr int kTileB = kBC * kRowB;   // bytes of one K or V tile
-  static constexpr int kCPT = kBC * kCPR / kNT;  // chunks per thread per tile
-  static_assert(kBC * kCPR % kNT == 0, "tile chunks must divide evenly over threads");
+  static constexpr int kStageB = 2 * kTileB;   // K tile + V tile
+  static constexpr int kDmaW = kBC * kCPR / (64 * NW);  // DMA loads per wave per tile
+  static constexpr int kLdsB = NBUF * kStageB;
+  static_assert(kBC * kCPR % (64 * NW) == 0, "tile chunks must divide evenly over waves");
   static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
+  static_assert(kLdsB <= 65536, "static LDS limit");
 };
 
 // LDS position (in 16-byte chunks) of chunk c of tile row r.  For 16-bit
 // types the XOR pattern makes both the 8-row column reads of K and the
 // 4-row x 32-byte transposing reads of V conflict-free; for fp32 it spreads
-// the 32-row column reads over 16 chunk positions.
+// the 32-row column reads over 16 chunk positions.  It is an involution in
+// c, so the same function maps an LDS position back to its global chunk.
+template <int CPR, bool F32>
+__device__ __forceinline__ int swz_f(int r) {
+  return F32 ? (r & 15) : (((r & 3) << 1) | ((r >> 2) & 1));
+}
 template <int CPR, bool F32>
 __device__ __forceinline__ int swz(int r, int c) {
-  const int f = F32 ? (r & 15) : (((r & 3) << 1) | ((r >> 2) & 1));
-  return r * CPR + (c ^ f);
+  return r * CPR + (c ^ swz_f<CPR, F32>(r));
 }
 
-template <typename T, int D, int QB, int KB, int NW, bool CAUSAL, bool VARLEN>
+// One 16-byte direct-to-LDS load per lane: LDS[m0 + 16*lane] <- buffer[voff].
+// Written as inline assembly because the compiler's own form makes every
+// later LDS read wait for all such loads; this kernel counts them itself.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, unsigned voff, unsigned m0) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Buffer resource for `bytes` bytes from `base` (raw, stride 0: offsets at or
+// beyond `bytes` read as zero).
+__device__ __forceinline__ u32x4_t make_rsrc(const char* base, unsigned bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+template <typename T, int D, int QB, int KB, int NW, int NBUF, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
-  using C = FwdCfg<T, D, QB, KB, NW>;
+  using C = FwdCfg<T, D, QB, KB, NW, NBUF>;
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr bool F32 = (E::kBytes == 4);
   constexpr int KS = D / E::kStep;        // MFMA steps over head_dim
   constexpr int DB = D / 32;              // 32-wide blocks of head_dim
   constexpr int TS = 32 / E::kStep;       // MFMA steps over a 32-key block
+  constexpr int L = 2 * C::kDmaW;         // DMA loads per wave per tile (K + V)
 
-  __shared__ u32x4_t smem[4 * C::kTileB / 16];   // [buffer][K, V][tile]
+  __shared__ __attribute__((aligned(16))) u32x4_t smem[C::kLdsB / 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -126,7 +176,33 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   const T* qp = (const T*)a.q + (size_t)q_tok0 * rs + (size_t)h * D;
   const char* kp = (const char*)((const T*)a.k + (size_t)k_tok0 * rs + (size_t)h * D);
   const char* vp = (const char*)((const T*)a.v + (size_t)k_tok0 * rs + (size_t)h * D);
-  const size_t rsb = rs * sizeof(T);
+  const unsigned rsb = (unsigned)(rs * sizeof(T));
+
+  // ---- tile loads: per-lane global offsets of the chunks this lane moves ----
+  unsigned voff[C::kDmaW];
+#pragma unroll
+  for (int u = 0; u < C::kDmaW; ++u) {
+    const int p = (u * NW + wave) * 64 + lane;  // LDS chunk position within the tile
+    const int r = p / C::kCPR, pos = p % C::kCPR;
+    voff[u] = (unsigned)r * rsb + (unsigned)((pos ^ swz_f<C::kCPR, F32>(r)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(size_t)(FA_LDS(char)*)smem;
+  auto issue = [&](int j) {
+    const int buf = j % NBUF;
+    const int rows = min(C::kBC, lk - j * C::kBC);
+    const u32x4_t rk = make_rsrc(kp + (size_t)j * C::kBC * rsb, (unsigned)rows * rsb);
+    const u32x4_t rv = make_rsrc(vp + (size_t)j * C::kBC * rsb, (unsigned)rows * rsb);
+    const unsigned kb0 = lds0 + buf * C::kStageB;
+#pragma unroll
+    for (int u = 0; u < C::kDmaW; ++u) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(kb0 + (u * NW + wave) * 1024);
+      dma16(rk, voff[u], m0);
+      dma16(rv, voff[u], m0 + C::kTileB);
+    }
+  };
+
+  // zero LDS once so no stale bit pattern can ever enter P V
+  for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
 
   // ---- Q block of this wave, held as MFMA B operands ----
   frag qf[QB][KS];
@@ -145,182 +221,211 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       }
     }
   }
+  // Q must be complete before the loop: its loads are the only vector-memory
+  // reads the compiler tracks, and a pending one would make it wait for all
+  // tile loads in flight at the first use inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x16_t oacc[DB][QB];
   float mrow[QB], lrow[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mrow[qb] = -INFINITY;  // running maximum, in units of scale*log2(e)
+    mrow[qb] = -INFINITY;  // running maximum (units of scale*log2 e); -inf: no key yet
     lrow[qb] = 0.f;        // running sum over this lane's keys
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db][qb] = f32x16_t{};
   }
+  __syncthreads();  // LDS zeroed before any tile lands
 
-  // ---- K/V tile staging: global -> registers -> LDS ----
-  u32x4_t kreg[C::kCPT], vreg[C::kCPT];
-  auto gload = [&](int j) {
 #pragma unroll
-    for (int u = 0; u < C::kCPT; ++u) {
-      const int id = tid + u * C::kNT;
-      const int r = id / C::kCPR, c = id % C::kCPR;
-      const int key = j * C::kBC + r;
-      if (key < lk) {
-        kreg[u] = *(const u32x4_t*)(kp + (size_t)key * rsb + c * 16);
-        vreg[u] = *(const u32x4_t*)(vp + (size_t)key * rsb + c * 16);
-      } else {
-        kreg[u] = u32x4_t{};  // rows past the end are zero: masked scores,
-        vreg[u] = u32x4_t{};  // and no 0 * garbage in P V
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nkt) issue(p);
+
+  // Lane parts of the LDS read addresses (byte offsets within a tile).  The
+  // swizzle term of a row depends only on the row's low bits, which these
+  // fix, so every other term of an address is a compile-time constant.
+  constexpr int RB = C::kCPR * 16;  // LDS bytes per tile row
+  int klane[KS];                    // K fragment of step ks, rows col (+32 kb)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if constexpr (F32) {
+      const int d = ks * 2 + hh;
+      klane[ks] = col * RB + ((d >> 2) ^ swz_f<C::kCPR, F32>(col)) * 16 + (d & 3) * 4;
+    } else {
+      klane[ks] = col * RB + ((ks * 2 + hh) ^ swz_f<C::kCPR, F32>(col)) * 16;
+    }
+  }
+  constexpr int NV = F32 ? 4 : DB;  // distinct lane parts of the V reads
+  int vlane[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if constexpr (F32) {
+      // row 4*hh + (t&3) (+ multiples of 8), column col of each 32-wide block
+      const int rr = 4 * hh + i;
+      vlane[i] = rr * RB + (((col >> 2) ^ (rr & 7)) * 16) + (col & 3) * 4;
+    } else {
+      // lane (16g + 4jj + qq) addresses V[4*hh + jj][32*db + 16*(g&1) + 4*qq .. +3]
+      const int g = lane >> 4, ii = lane & 15, jj = ii >> 2, qq = ii & 3;
+      const int rr = 4 * hh + jj;
+      const int ch = 4 * i + 2 * (g & 1) + (qq >> 1);
+      vlane[i] = rr * RB + ((ch ^ swz_f<C::kCPR, F32>(rr)) * 16) + (qq & 1) * 8;
+    }
+  }
+
+  auto tile = [&](int j, bool need_mask) {
+    const int k0 = j * C::kBC;
+    const int sb = (j % NBUF) * C::kStageB;  // byte offset of this tile's K in LDS
+    const char* kt = (const char*)smem + sb;
+    const int vt_off = sb + C::kTileB;
+
+    // S^T = K Q^T for KB key blocks x QB query blocks, then x = c S - m
+    f32x16_t sacc[KB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const frag kf = *(const frag*)(kt + klane[ks] + kb * 32 * RB);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sacc[kb][qb] = mma(kf, qf[qb][ks], sacc[kb][qb]);
+      }
+    }
+    {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float ms = mrow[qb] == -INFINITY ? 0.f : mrow[qb];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = __builtin_fmaf(sacc[kb][qb][r], a.c, -ms);
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qi = wq0 + qb * 32 + col;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key >= lk || (CAUSAL && key > qi + off)) sacc[kb][qb][r] = -INFINITY;
+          }
+        }
+    }
+
+    // tile maximum relative to the running one; lazy rescale when needed
+    float mx[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[kb][qb][r]);
+      mx[qb] = half_max(m);
+      need |= (mx[qb] > kTau) || (mrow[qb] == -INFINITY && mx[qb] != -INFINITY);
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool fresh = mrow[qb] == -INFINITY;
+        float delta;
+        if (fresh) delta = mx[qb] == -INFINITY ? 0.f : mx[qb];
+        else delta = mx[qb] > kTau ? mx[qb] : 0.f;
+        const float mold = fresh ? 0.f : mrow[qb];
+        const float mnew = mold + delta;
+        const float alpha = fresh ? 0.f : fast_exp2(-delta);
+        mrow[qb] = (fresh && mx[qb] == -INFINITY) ? -INFINITY : mnew;
+        lrow[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][qb][r] -= delta;
+      }
+    }
+
+    // probabilities (packed as the P V operand) and running sums, each
+    // 16-key slice feeding its P V products at once
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < TS; ++t) {
+        frag pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          if constexpr (F32) {
+            const float p = fast_exp2(sacc[kb][qb][t]);
+            lrow[qb] += p;
+            pf[qb] = p;
+          } else {
+            u32x4_t u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = fast_exp2(sacc[kb][qb][8 * t + 2 * e]);
+              const float p1 = fast_exp2(sacc[kb][qb][8 * t + 2 * e + 1]);
+              lrow[qb] += p0;  // the sum takes the unrounded fp32 probabilities
+              lrow[qb] += p1;
+              u[e] = pack2(p0, p1, (T*)nullptr);
+            }
+            pf[qb] = __builtin_bit_cast(frag, u);
+          }
+        }
+        // O^T += V^T P^T for this slice
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          frag vf;
+          if constexpr (F32) {
+            // key kb*32 + 8*(t>>2) + 4*hh + (t&3); its swizzle adds 8*((t>>2)&1)
+            // to the chunk index of column 32*db + col
+            const int cx = (32 * db / 4) ^ (8 * ((t >> 2) & 1));
+            vf = *(const float*)((const char*)smem + vt_off + vlane[t & 3] +
+                                 (kb * 32 + 8 * (t >> 2)) * RB + cx * 16);
+          } else {
+            // the transposing read hands lane (16g + i) the 4 keys at column d0 + i
+            const int base = vt_off + vlane[db] + (kb * 32 + 16 * t) * RB;
+            s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + base));
+            s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + base + 8 * RB));
+            const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+            const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+            const u32x4_t u = {lo2.x, lo2.y, hi2.x, hi2.y};
+            vf = __builtin_bit_cast(frag, u);
+          }
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mma(vf, pf[qb], oacc[db][qb]);
+        }
       }
     }
   };
-  auto sstore = [&](int buf) {
-    u32x4_t* kt = smem + buf * (2 * C::kTileB / 16);
-    u32x4_t* vt = kt + C::kTileB / 16;
-#pragma unroll
-    for (int u = 0; u < C::kCPT; ++u) {
-      const int id = tid + u * C::kNT;
-      const int r = id / C::kCPR, c = id % C::kCPR;
-      kt[swz<C::kCPR, F32>(r, c)] = kreg[u];
-      vt[swz<C::kCPR, F32>(r, c)] = vreg[u];
-    }
-  };
-
-  if (nkt > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
 
   for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) gload(j + 1);
+    // tile j has landed once at most the loads of later tiles are pending
+    if (j + NBUF - 2 < nkt) {
+      if constexpr (NBUF >= 3) vm_wait<L * (NBUF - 2)>();
+      else vm_wait<0>();
+    } else {
+      vm_wait<0>();
+    }
+    __syncthreads();  // every wave's share of tile j is in; tile j-1's buffer is free
+    if (j + NBUF - 1 < nkt) issue(j + NBUF - 1);
     const int k0 = j * C::kBC;
     const bool active = (wq_last >= wq0) && (!CAUSAL || k0 <= wq_last + off);
     if (active) {
       const bool need_mask = (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > wq0 + off);
-      const char* kt = (const char*)(smem + buf * (2 * C::kTileB / 16));
-      const int vt_off = buf * 2 * C::kTileB + C::kTileB;  // byte offset of the V tile
-
-      // S^T = K Q^T for KB key blocks x QB query blocks
-      f32x16_t sacc[KB][QB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int r = kb * 32 + col;
-          frag kf;
-          if constexpr (F32) {
-            const int d = ks * 2 + hh;
-            kf = *(const float*)(kt + swz<C::kCPR, F32>(r, d >> 2) * 16 + (d & 3) * 4);
-          } else {
-            kf = *(const frag*)(kt + swz<C::kCPR, F32>(r, ks * 2 + hh) * 16);
-          }
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mma(kf, qf[qb][ks], sacc[kb][qb]);
-        }
-      }
-
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int qi = wq0 + qb * 32 + col;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-              if (key >= lk || (CAUSAL && key > qi + off)) sacc[kb][qb][r] = -INFINITY;
-            }
-          }
-      }
-
-      // online softmax: new maximum, rescale, probabilities, running sum
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-        mx = half_max(mx);
-        const float tmc = (mx == -INFINITY) ? -INFINITY : mx * a.c;
-        const float mnew = fmaxf(mrow[qb], tmc);
-        const float ms = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = fast_exp2(mrow[qb] - ms);
-        mrow[qb] = mnew;
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float s = sacc[kb][qb][r];
-            float p = fast_exp2(__builtin_fmaf(s, a.c, -ms));
-            if (need_mask && s == -INFINITY) p = 0.f;
-            sacc[kb][qb][r] = p;
-            ps += p;
-          }
-        lrow[qb] = lrow[qb] * alpha + ps;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
-      }
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int t = 0; t < TS; ++t) {
-          frag pf[QB];
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            if constexpr (F32) {
-              pf[qb] = sacc[kb][qb][t];
-            } else {
-              u32x4_t u;
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                u[e] = pack2(sacc[kb][qb][8 * t + 2 * e], sacc[kb][qb][8 * t + 2 * e + 1], (T*)nullptr);
-              pf[qb] = __builtin_bit_cast(frag, u);
-            }
-          }
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            frag vf;
-            if constexpr (F32) {
-              const int row = kb * 32 + 8 * (t >> 2) + 4 * hh + (t & 3);
-              const int d = 32 * db + col;
-              vf = *(const float*)((const char*)smem + vt_off +
-                                   swz<C::kCPR, F32>(row, d >> 2) * 16 + (d & 3) * 4);
-            } else {
-              // lane (16g + 4jj + qq) addresses V[row0 + jj][d0 + 4qq .. +3]; the
-              // transposing read hands lane (16g + i) the 4 keys at column d0 + i.
-              const int g = lane >> 4, ii = lane & 15, jj = ii >> 2, qq = ii & 3;
-              const int row = kb * 32 + 16 * t + 4 * hh + jj;
-              const int d = 32 * db + 16 * (g & 1) + 4 * qq;
-              const int b0 = vt_off + swz<C::kCPR, F32>(row, d >> 3) * 16 + (qq & 1) * 8;
-              const int b1 = vt_off + swz<C::kCPR, F32>(row + 8, d >> 3) * 16 + (qq & 1) * 8;
-              s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + b0));
-              s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + b1));
-              u32x4_t u = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                           __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
-              vf = __builtin_bit_cast(frag, u);
-            }
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mma(vf, pf[qb], oacc[db][qb]);
-          }
-        }
-      }
+      tile(j, need_mask);
     }
-    if (j + 1 < nkt) sstore(buf ^ 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: O = O / l, lse = m + ln l ----
+  // ---- epilogue: O = O / l, lse = m + log2 l (converted to natural log) ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = half_sum(lrow[qb]);
@@ -435,27 +540,31 @@ hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int 
 // ---------------------------------------------------------------------------
 // Instances and dispatch
 // ---------------------------------------------------------------------------
-// (QB, KB, NW) per element type and head_dim.
+// (QB, KB, NW, NBUF) per element type and head_dim.
 template <typename T, int D> struct Tile;
-template <> struct Tile<__bf16, 64> { static constexpr int QB = 2, KB = 2, NW = 4; };
-template <> struct Tile<_Float16, 64> { static constexpr int QB = 2, KB = 2, NW = 4; };
-template <> struct Tile<__bf16, 128> { static constexpr int QB = 1, KB = 2, NW = 4; };
-template <> struct Tile<_Float16, 128> { static constexpr int QB = 1, KB = 2, NW = 4; };
-template <> struct Tile<float, 64> { static constexpr int QB = 1, KB = 2, NW = 4; };
-template <> struct Tile<float, 128> { static constexpr int QB = 1, KB = 1, NW = 4; };
+template <> struct Tile<__bf16, 64> { static constexpr int QB = 2, KB = 2, NW = 4, NBUF = 4; };
+template <> struct Tile<_Float16, 64> { static constexpr int QB = 2, KB = 2, NW = 4, NBUF = 4; };
+template <> struct Tile<__bf16, 128> { static constexpr int QB = 1, KB = 2, NW = 4, NBUF = 2; };
+template <> struct Tile<_Float16, 128> { static constexpr int QB = 1, KB = 2, NW = 4, NBUF = 2; };
+template <> struct Tile<float, 64> { static constexpr int QB = 1, KB = 2, NW = 4, NBUF = 2; };
+template <> struct Tile<float, 128> { static constexpr int QB = 1, KB = 1, NW = 4, NBUF = 2; };
 
 template <typename T, int D>
 static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned grid,
                            hipStream_t stream) {
   using Tl = Tile<T, D>;
-  constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW;
+  constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF;
   dim3 g(grid), blk(NW * 64);
   if (causal) {
-    if (varlen) hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, true, true>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, true, false>), g, blk, 0, stream, a);
+    if (varlen)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, true, true>), g, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, true, false>), g, blk, 0, stream, a);
   } else {
-    if (varlen) hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, false, true>), g, blk, 0, stream, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, false, false>), g, blk, 0, stream, a);
+    if (varlen)
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, false, true>), g, blk, 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, false, false>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
 }
