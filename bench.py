@@ -130,8 +130,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one call only (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="time one call only (for profiling runs); 'copy' runs a plain "
+                         "1 GiB device-to-device copy, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "
@@ -145,6 +146,14 @@ def main():
     fa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "copy":
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "calls": args.warmup + args.steps}))
+        return
     wp, wd = wl.CFG[3], wl.CFG[5]
     do_p = args.only in (None, "prefill")
     do_d = args.only in (None, "decode")

@@ -40,24 +40,28 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source and link ``out``; ``defines`` are extra -D flags
+    (tile-shape overrides for tuning builds)."""
+    bdir = os.path.join(BUILD, os.path.basename(out) + ".objs")
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     cmds = []
+    extra = ["-D" + d for d in defines]
     for src in SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         objs.append(obj)
-        cmds.append([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

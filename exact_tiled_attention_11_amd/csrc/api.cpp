@@ -107,8 +107,11 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
   if (nseq < 1 || total_q < 0) return 0;
-  // the largest query block of any instance bounds the tile count from above
-  const int rows = 128;
+  // the smallest query block of any instance bounds the tile count from above
+  int rows = fa::fwd_block_rows(FA_F32, 64);
+  const fa_dtype_t dts[3] = {FA_F32, FA_F16, FA_BF16};
+  for (fa_dtype_t dt : dts)
+    for (int d = 64; d <= 128; d += 64) rows = rows < fa::fwd_block_rows(dt, d) ? rows : fa::fwd_block_rows(dt, d);
   return fa::varlen_sched_bytes(nseq, fa::varlen_max_tiles(nseq, total_q, rows));
 }
 

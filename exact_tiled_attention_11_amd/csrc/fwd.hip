@@ -22,11 +22,12 @@
 //  * Q stays in VGPRs as the MFMA B operand for the whole kernel; one FMA
 //    per score forms the exp2 exponent c*s - m (c = scale*log2 e), so a
 //    probability costs an FMA and a v_exp_f32.
-//  * The running maximum is raised lazily: only when a tile's maximum
-//    exceeds it by more than kTau (or on a row's first visible key) are the
-//    accumulator, the sum and the exponents rescaled; otherwise p <= 2^kTau.
-//    The result is the same softmax, since the final division uses the same
-//    offset as every exponent.
+//  * The running maximum is raised lazily: a tile is first exponentiated
+//    with the current offset, and only if a row's tile sum shows a
+//    probability that could exceed 2^15 (or the row has not seen a key yet)
+//    is the tile maximum taken, the accumulator and sum rescaled and the tile
+//    redone.  The result is the same softmax, since the final division uses
+//    the same offset as every exponent; the common path needs no maximum.
 //  * K and V tiles of KB*32 keys reach LDS through direct buffer loads
 //    (buffer_load_dwordx4 ... lds, no VGPR staging), NBUF tiles deep, with
 //    an XOR swizzle over 16-byte chunks chosen per lane on the global side.
@@ -51,7 +52,8 @@
 
 namespace fa {
 
-// Exponent headroom of the lazy maximum: probabilities stay below 2^kTau.
+// A tile whose maximum exceeds the running offset by more than kTau (in
+// exp2 units) raises the offset once the lazy check has fired.
 constexpr float kTau = 8.0f;
 
 template <typename T, int D, int QB, int KB, int NW, int NBUF>
@@ -69,7 +71,8 @@ struct FwdCfg {
   static constexpr int kLdsB = NBUF * kStageB;
   static_assert(kBC * kCPR % (64 * NW) == 0, "tile chunks must divide evenly over waves");
   static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
-  static_assert(kLdsB <= 65536, "static LDS limit");
+  static_assert(kLdsB <= 160 * 1024, "LDS per workgroup");
+  static_assert(NBUF >= 2, "at least one tile in flight");
 };
 
 // LDS position (in 16-byte chunks) of chunk c of tile row r.  For 16-bit
@@ -111,8 +114,8 @@ __device__ __forceinline__ u32x4_t make_rsrc(const char* base, unsigned bytes) {
   return r;
 }
 
-template <typename T, int D, int QB, int KB, int NW, int NBUF, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, int QB, int KB, int NW, int NBUF, int OCC, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, D, QB, KB, NW, NBUF>;
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
   constexpr int TS = 32 / E::kStep;       // MFMA steps over a 32-key block
   constexpr int L = 2 * C::kDmaW;         // DMA loads per wave per tile (K + V)
 
-  __shared__ __attribute__((aligned(16))) u32x4_t smem[C::kLdsB / 16];
+  extern __shared__ __attribute__((aligned(16))) u32x4_t smem[];  // C::kLdsB bytes
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,29 +275,38 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  auto tile = [&](int j, bool need_mask) {
-    const int k0 = j * C::kBC;
-    const int sb = (j % NBUF) * C::kStageB;  // byte offset of this tile's K in LDS
-    const char* kt = (const char*)smem + sb;
-    const int vt_off = sb + C::kTileB;
+  f32x16_t sacc[KB][QB];      // scores of the tile being processed
 
-    // S^T = K Q^T for KB key blocks x QB query blocks, then x = c S - m
-    f32x16_t sacc[KB][QB];
+  auto active = [&](int j) -> bool {
+    return j >= 0 && j < nkt && wq_last >= wq0 && (!CAUSAL || j * C::kBC <= wq_last + off);
+  };
+
+  auto scores = [&](int j) {
+    {
+      const int sb = (j % NBUF) * C::kStageB;  // byte offset of this tile's K in LDS
+      const char* kt = (const char*)smem + sb;
+      // S^T = K Q^T for KB key blocks x QB query blocks
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16_t{};
+        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16_t{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const frag kf = *(const frag*)(kt + klane[ks] + kb * 32 * RB);
+        for (int kb = 0; kb < KB; ++kb) {
+          const frag kf = *(const frag*)(kt + klane[ks] + kb * 32 * RB);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          sacc[kb][qb] = mma(kf, qf[qb][ks], sacc[kb][qb]);
+          for (int qb = 0; qb < QB; ++qb)
+            sacc[kb][qb] = mma(kf, qf[qb][ks], sacc[kb][qb]);
+        }
       }
     }
-    {
+  };
+
+  auto softmax = [&](int j) {
+    const int k0 = j * C::kBC;
+    const bool need_mask = (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > wq0 + off);
+    {  // x = c S - m
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float ms = mrow[qb] == -INFINITY ? 0.f : mrow[qb];
@@ -305,80 +317,99 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
       }
     }
     if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qi = wq0 + qb * 32 + col;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key >= lk || (CAUSAL && key > qi + off)) sacc[kb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // tile maximum relative to the running one; lazy rescale when needed
-    float mx[QB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[kb][qb][r]);
-      mx[qb] = half_max(m);
-      need |= (mx[qb] > kTau) || (mrow[qb] == -INFINITY && mx[qb] != -INFINITY);
-    }
-    if (__any(need)) {
+      // A masked score becomes -2^109 or less: exp2 gives 0 and it never wins a
+      // maximum.  Key kb*32 + 8*(r>>2) + 4*hh + (r&3) of the tile is visible to
+      // query qi iff 8*(r>>2) + (r&3) <= lim, with lim below; the test is one
+      // FMA and one min per score (no lane masks).
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bool fresh = mrow[qb] == -INFINITY;
-        float delta;
-        if (fresh) delta = mx[qb] == -INFINITY ? 0.f : mx[qb];
-        else delta = mx[qb] > kTau ? mx[qb] : 0.f;
-        const float mold = fresh ? 0.f : mrow[qb];
-        const float mnew = mold + delta;
-        const float alpha = fresh ? 0.f : fast_exp2(-delta);
-        mrow[qb] = (fresh && mx[qb] == -INFINITY) ? -INFINITY : mnew;
-        lrow[qb] *= alpha;
+        const int qi = wq0 + qb * 32 + col;
+        const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;  // last visible key
 #pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+        for (int kb = 0; kb < KB; ++kb) {
+          const float lim = (float)(last - k0 - kb * 32 - 4 * hh);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][qb][r] -= delta;
+          for (int r = 0; r < 16; ++r) {
+            const float cr = (float)(8 * (r >> 2) + (r & 3));
+            sacc[kb][qb][r] = fminf(sacc[kb][qb][r], __builtin_fmaf(lim, 0x1p110f, (0.5f - cr) * 0x1p110f));
+          }
+        }
       }
     }
 
-    // probabilities (packed as the P V operand) and running sums, each
-    // 16-key slice feeding its P V products at once
+    // Key block by key block: probabilities (packed as the P V operand) and
+    // row sums over the unrounded fp32 values (the log-sum-exp needs that
+    // precision), then that block's P V products.
+    const int vt_off = (j % NBUF) * C::kStageB + C::kTileB;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      frag pk[TS][QB];
+      float tsum[QB];
+      auto probs = [&]() {
 #pragma unroll
-      for (int t = 0; t < TS; ++t) {
-        frag pf[QB];
+        for (int qb = 0; qb < QB; ++qb) tsum[qb] = 0.f;
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            if constexpr (F32) {
+              const float p = fast_exp2(sacc[kb][qb][t]);
+              tsum[qb] += p;
+              pk[t][qb] = p;
+            } else {
+              u32x4_t u;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(sacc[kb][qb][8 * t + 2 * e]);
+                const float p1 = fast_exp2(sacc[kb][qb][8 * t + 2 * e + 1]);
+                tsum[qb] += p0;
+                tsum[qb] += p1;
+                u[e] = pack2(p0, p1, (T*)nullptr);
+              }
+              pk[t][qb] = __builtin_bit_cast(frag, u);
+            }
+          }
+      };
+      probs();
+
+      // Lazy maximum: the offset m stays unless a probability could exceed
+      // 2^15 (seen in this lane's block sum) or the row has not seen a key
+      // yet; then the block maximum is taken, m raised, the accumulated
+      // output and sum rescaled, and the block redone.
+      bool need = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) need |= (mrow[qb] == -INFINITY) || !(tsum[qb] <= 0x1p15f);
+      if (__any(need)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          if constexpr (F32) {
-            const float p = fast_exp2(sacc[kb][qb][t]);
-            lrow[qb] += p;
-            pf[qb] = p;
-          } else {
-            u32x4_t u;
+          float m = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 = fast_exp2(sacc[kb][qb][8 * t + 2 * e]);
-              const float p1 = fast_exp2(sacc[kb][qb][8 * t + 2 * e + 1]);
-              lrow[qb] += p0;  // the sum takes the unrounded fp32 probabilities
-              lrow[qb] += p1;
-              u[e] = pack2(p0, p1, (T*)nullptr);
-            }
-            pf[qb] = __builtin_bit_cast(frag, u);
-          }
+          for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[kb][qb][r]);
+          const float mx = half_max(m);
+          const bool fresh = mrow[qb] == -INFINITY;
+          const bool none = !(mx > -1e30f);  // no visible key in this block
+          float delta;
+          if (fresh) delta = none ? 0.f : mx;
+          else delta = mx > kTau ? mx : 0.f;
+          const float mold = fresh ? 0.f : mrow[qb];
+          const float alpha = fresh ? 0.f : fast_exp2(-delta);
+          mrow[qb] = (fresh && none) ? -INFINITY : mold + delta;
+          lrow[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
+#pragma unroll
+          for (int k2 = kb; k2 < KB; ++k2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[k2][qb][r] -= delta;
         }
-        // O^T += V^T P^T for this slice
+        probs();
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) lrow[qb] += tsum[qb];
+
+      // O^T += V^T P^T for this key block
+#pragma unroll
+      for (int t = 0; t < TS; ++t) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           frag vf;
@@ -401,27 +432,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_kernel(FwdArgs a) {
             vf = __builtin_bit_cast(frag, u);
           }
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mma(vf, pf[qb], oacc[db][qb]);
+          for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mma(vf, pk[t][qb], oacc[db][qb]);
         }
       }
     }
   };
 
+
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nkt) issue(p);
+
   for (int j = 0; j < nkt; ++j) {
-    // tile j has landed once at most the loads of later tiles are pending
-    if (j + NBUF - 2 < nkt) {
-      if constexpr (NBUF >= 3) vm_wait<L * (NBUF - 2)>();
-      else vm_wait<0>();
-    } else {
-      vm_wait<0>();
-    }
+    // tile j has landed once at most the loads of the later tiles already
+    // issued (up to NBUF - 2 of them) are pending
+    const int later = min(NBUF - 2, nkt - 1 - j);
+    if (later >= 2) vm_wait<2 * L>();
+    else if (later == 1) vm_wait<L>();
+    else vm_wait<0>();
     __syncthreads();  // every wave's share of tile j is in; tile j-1's buffer is free
     if (j + NBUF - 1 < nkt) issue(j + NBUF - 1);
-    const int k0 = j * C::kBC;
-    const bool active = (wq_last >= wq0) && (!CAUSAL || k0 <= wq_last + off);
-    if (active) {
-      const bool need_mask = (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > wq0 + off);
-      tile(j, need_mask);
+    if (active(j)) {
+      scores(j);
+      softmax(j);
     }
   }
 
@@ -540,33 +573,51 @@ hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int 
 // ---------------------------------------------------------------------------
 // Instances and dispatch
 // ---------------------------------------------------------------------------
-// (QB, KB, NW, NBUF) per element type and head_dim.
+// (QB, KB, NW, NBUF, OCC) per element type and head_dim: query blocks of 32
+// per wave, key blocks of 32 per tile, waves per workgroup, tiles in flight,
+// and the waves per SIMD the register budget is sized for.
+#ifndef FA_TILE_16_64
+#define FA_TILE_16_64 1, 2, 4, 2, 4
+#endif
+#ifndef FA_TILE_16_128
+#define FA_TILE_16_128 1, 2, 4, 2, 2
+#endif
+template <int QB_, int KB_, int NW_, int NBUF_, int OCC_>
+struct TileCfg {
+  static constexpr int QB = QB_, KB = KB_, NW = NW_, NBUF = NBUF_, OCC = OCC_;
+};
 template <typename T, int D> struct Tile;
-template <> struct Tile<__bf16, 64> { static constexpr int QB = 2, KB = 2, NW = 4, NBUF = 4; };
-template <> struct Tile<_Float16, 64> { static constexpr int QB = 2, KB = 2, NW = 4, NBUF = 4; };
-template <> struct Tile<__bf16, 128> { static constexpr int QB = 1, KB = 2, NW = 4, NBUF = 2; };
-template <> struct Tile<_Float16, 128> { static constexpr int QB = 1, KB = 2, NW = 4, NBUF = 2; };
-template <> struct Tile<float, 64> { static constexpr int QB = 1, KB = 2, NW = 4, NBUF = 2; };
-template <> struct Tile<float, 128> { static constexpr int QB = 1, KB = 1, NW = 4, NBUF = 2; };
+template <> struct Tile<__bf16, 64> : TileCfg<FA_TILE_16_64> {};
+template <> struct Tile<_Float16, 64> : TileCfg<FA_TILE_16_64> {};
+template <> struct Tile<__bf16, 128> : TileCfg<FA_TILE_16_128> {};
+template <> struct Tile<_Float16, 128> : TileCfg<FA_TILE_16_128> {};
+template <> struct Tile<float, 64> : TileCfg<1, 2, 4, 2, 2> {};
+template <> struct Tile<float, 128> : TileCfg<1, 1, 4, 2, 2> {};
+
+template <typename K>
+static hipError_t launch_k(K kern, unsigned grid, int threads, int lds, hipStream_t stream,
+                           const FwdArgs& a) {
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, stream, a);
+  return hipGetLastError();
+}
 
 template <typename T, int D>
 static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned grid,
                            hipStream_t stream) {
   using Tl = Tile<T, D>;
-  constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF;
-  dim3 g(grid), blk(NW * 64);
+  constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;
+  constexpr int lds = FwdCfg<T, D, QB, KB, NW, NB>::kLdsB;
   if (causal) {
-    if (varlen)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, true, true>), g, blk, 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, true, false>), g, blk, 0, stream, a);
-  } else {
-    if (varlen)
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, false, true>), g, blk, 0, stream, a);
-    else
-      hipLaunchKernelGGL((fwd_kernel<T, D, QB, KB, NW, NB, false, false>), g, blk, 0, stream, a);
+    if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, true, true>, grid, NW * 64, lds, stream, a);
+    return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, true, false>, grid, NW * 64, lds, stream, a);
   }
-  return hipGetLastError();
+  if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, false, true>, grid, NW * 64, lds, stream, a);
+  return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, false, false>, grid, NW * 64, lds, stream, a);
 }
 
 template <typename T, int D> static int rows_t() { return Tile<T, D>::NW * 32 * Tile<T, D>::QB; }
