@@ -1,0 +1,129 @@
+"""GPU parity at the benchmark workloads' full sizes, in the launch configuration bench.py times.
+
+The oracle cannot finish whole workloads of this size in a test, so each case compares sampled
+output rows (chosen at random plus tile boundaries and the first/last rows) with the oracle
+computed row by row, and checks properties that hold at any size on every row: all outputs
+finite, every causal row has a finite log-sum-exp, and two runs are bit-identical.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _fa():
+    import exact_tiled_attention_11_amd as fa
+    fa.load()
+    return fa
+
+
+def _sample_rows(rng, n, extra=()):
+    base = {0, 1, n - 1, n // 2}
+    for t in (63, 64, 127, 128, 255, 256, 511, 512):
+        if t < n:
+            base.add(t)
+    base.update(int(x) for x in extra if 0 <= x < n)
+    base.update(int(x) for x in rng.integers(0, n, size=24))
+    return sorted(base)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_prefill_full_size_sampled(cfg):
+    fa = _fa()
+    w = wl.CFG[cfg]
+    say("generate %s" % w.name)
+    q, k, v = wl.prefill_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    say("fa_fwd %s" % w.name)
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    o2, lse2 = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(1000 + cfg)
+    pairs = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
+    for b, h in pairs:
+        rows = _sample_rows(rng, w.Nq)
+        kb, vb = wl.to_f64(k[b, :, h]), wl.to_f64(v[b, :, h])
+        qr = wl.to_f64(q[b, rows, h])
+        o_ref, lse_ref = oracle.attention_rows(qr, rows, kb, vb, w.Nq, w.Nk, w.scale, w.causal)
+        assert_close(w.dtype, wl.to_f64(o_c[b, rows, h]), o_ref, lse_c[b, h, rows].double().numpy(),
+                     lse_ref, "%s b%d h%d" % (w.name, b, h))
+
+
+def test_varlen_full_size_sampled():
+    fa = _fa()
+    w = wl.CFG[4]
+    say("generate %s" % w.name)
+    q, k, v, cu = wl.varlen_inputs(w)
+    cud = torch.from_numpy(cu).cuda()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    say("fa_fwd_varlen %s" % w.name)
+    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(1004)
+    lens = np.diff(cu)
+    for s in range(len(lens)):
+        h = int(rng.integers(w.H))
+        a0, L = int(cu[s]), int(lens[s])
+        rows = _sample_rows(rng, L)
+        kb, vb = wl.to_f64(k[a0:a0 + L, h]), wl.to_f64(v[a0:a0 + L, h])
+        qr = wl.to_f64(q[[a0 + r for r in rows], h])
+        o_ref, lse_ref = oracle.attention_rows(qr, rows, kb, vb, L, L, w.scale, True)
+        got = wl.to_f64(o_c[[a0 + r for r in rows], h])
+        assert_close(w.dtype, got, o_ref, lse_c[h, [a0 + r for r in rows]].double().numpy(), lse_ref,
+                     "%s seq%d h%d" % (w.name, s, h))
+
+
+def test_decode_full_size_sampled():
+    fa = _fa()
+    w = wl.CFG[5]
+    lens = w.lengths()
+    say("generate %s (device caches %.1f GB each)" % (w.name, w.B * w.Nk * w.H * w.D * 2 / 1e9))
+    q = wl.decode_query(w)
+    kc = torch.empty((w.B, w.Nk, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    for b in range(w.B):
+        L = int(lens[b])
+        kc[b, :L].copy_(wl.decode_cache_rows(w, 1, b, L))
+        vc[b, :L].copy_(wl.decode_cache_rows(w, 2, b, L))
+        # rows past the length must never be read: fill a band of them with NaN
+        kc[b, L:min(w.Nk, L + 300)] = float("nan")
+        vc[b, L:min(w.Nk, L + 300)] = float("nan")
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    say("fa_decode_splitkv %s" % w.name)
+    o, lse = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=w.chunk)
+    o2, lse2 = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    del kc, vc
+    rng = np.random.default_rng(1005)
+    bs = sorted({0, w.B - 1, int(np.argmax(lens)), int(np.argmin(lens))} | {int(x) for x in rng.integers(0, w.B, 4)})
+    for b in bs:
+        L = int(lens[b])
+        kb = wl.to_f64(wl.decode_cache_rows(w, 1, b, L))
+        vb = wl.to_f64(wl.decode_cache_rows(w, 2, b, L))
+        for h in sorted({0, w.H - 1, int(rng.integers(w.H))}):
+            o_ref, lse_ref = oracle.attention_rows(wl.to_f64(q[b, h])[None], [0], kb[:, h], vb[:, h], 1,
+                                                   L, w.scale, False)
+            assert_close(w.dtype, wl.to_f64(o_c[b, h])[None], o_ref, lse_c[b, h:h + 1].double().numpy(),
+                         lse_ref, "%s b%d h%d" % (w.name, b, h))
