@@ -12,16 +12,19 @@
 //
 // gfx950 mapping (ours):
 //  * partial kernel: one workgroup of chunk/64 waves per (batch, chunk,
-//    head) work item, taken in a grid-stride loop ordered chunk-major so
-//    that workgroups running together read the contiguous all-heads stretch
+//    head) work item, numbered chunk-major with heads fastest so that
+//    workgroups dispatched together read the contiguous all-heads stretch
 //    of the cache.  Each wave issues every 16-byte K and V load of its 64
 //    keys up front (up to 32 KB in flight per wave) — the path is bound by
 //    HBM bandwidth, so the VALU work (dot products, exp2, P·V) is kept
 //    simple and overlapped by the loads of other waves.
 //  * combine kernel: one wave per (batch, head) merges the chunk summaries
-//    in chunk order; the result is bit-reproducible.
+//    in chunk order, with the loads of eight chunks in flight together; the
+//    result is bit-reproducible.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "fa_device.h"
 #include "launch.h"
@@ -96,13 +99,21 @@ __device__ __forceinline__ void axpy(float* o, float p, const u32x4_t& v, float*
   for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(p, __uint_as_float(v[e]), o[e]);
 }
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void decode_partial_kernel(DecodeArgs a) {
+// Cache rows are read exactly once per call: non-temporal loads keep them
+// from displacing reusable lines (measured about 6 % faster than plain loads).
+__device__ __forceinline__ u32x4_t stream_load(const u32x4_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// NW waves of KPW keys each cover one chunk of NW*KPW keys.
+template <typename T, int D, int NW, int KPW>
+__global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeArgs a) {
   constexpr int ES = Elem<T>::kBytes;
   constexpr int EPL = 16 / ES;          // elements per 16-byte slice
   constexpr int LPK = D * ES / 16;      // lanes per key row
   constexpr int KPI = 64 / LPK;         // keys per wave-wide load
-  constexpr int NI = 64 / KPI;          // loads per lane for 64 keys
+  constexpr int NI = KPW / KPI;         // loads per lane for the wave's keys
+  static_assert(KPW % KPI == 0, "keys per wave must fill whole loads");
   static_assert(LPK == 8 || LPK == 16 || LPK == 32, "unsupported row width");
 
   __shared__ float red_m[NW];
@@ -115,18 +126,17 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_partial_kernel(DecodeArgs a
   const int kk = lane / LPK;            // key slot within a wave-wide load
   const int dd = lane % LPK;            // 16-byte slice of the row
 
-  const int items = a.NC * a.B * a.H;   // host guarantees < 2^31
   const size_t rs = (size_t)a.H * D;    // elements between cache rows
-
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+  {
+    const int it = blockIdx.x;          // host guarantees NC*B*H < 2^31
     const int cb = it / a.H;
     const int h = it - cb * a.H;
     const int c = cb / a.B;
     const int b = cb - c * a.B;
     const int lk = min(max(a.seqlens_k[b], 0), a.Nk_max);
-    if (c * a.chunk >= lk) continue;    // uniform over the workgroup
+    if (c * a.chunk >= lk) return;      // uniform over the workgroup
 
-    const int key0 = c * a.chunk + wave * 64;
+    const int key0 = c * a.chunk + wave * KPW;
     const char* kb = (const char*)((const T*)a.kc + (size_t)b * a.Nk_max * rs + (size_t)h * D) + dd * 16;
     const char* vb = (const char*)((const T*)a.vc + (size_t)b * a.Nk_max * rs + (size_t)h * D) + dd * 16;
     u32x4_t kr[NI], vr[NI];
@@ -134,8 +144,8 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_partial_kernel(DecodeArgs a
     for (int i = 0; i < NI; ++i) {
       const int key = key0 + i * KPI + kk;
       if (key < lk) {
-        kr[i] = *(const u32x4_t*)(kb + (size_t)key * rs * ES);
-        vr[i] = *(const u32x4_t*)(vb + (size_t)key * rs * ES);
+        kr[i] = stream_load((const u32x4_t*)(kb + (size_t)key * rs * ES));
+        vr[i] = stream_load((const u32x4_t*)(vb + (size_t)key * rs * ES));
       } else {
         kr[i] = u32x4_t{};
         vr[i] = u32x4_t{};
@@ -225,23 +235,24 @@ __global__ __launch_bounds__(NW * 64, 2) void decode_partial_kernel(DecodeArgs a
       a.ws_ml[rec * 2 + 0] = M;
       a.ws_ml[rec * 2 + 1] = s;
     }
-    __syncthreads();  // LDS is reused by the next work item
   }
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int DPL = (D + 63) / 64;  // output elements per lane
+  constexpr int DPL = D / 64;  // output elements per lane (1 or 2), loaded together
+  constexpr int U = 8;         // chunks whose loads are issued together
+  using vec = typename std::conditional<DPL == 2, float2, float>::type;
   const int lane = threadIdx.x;
   const int bh = blockIdx.x;
   const int b = bh / a.H;
   const int lk = min(max(a.seqlens_k[b], 0), a.Nk_max);
   const int nck = (lk + a.chunk - 1) / a.chunk;
-  const float* ml = a.ws_ml + (size_t)bh * a.NC * 2;
-  const float* po = a.ws_o + (size_t)bh * a.NC * D;
+  const float2* ml = (const float2*)(a.ws_ml + (size_t)bh * a.NC * 2);
+  const vec* po = (const vec*)(a.ws_o + (size_t)bh * a.NC * D) + lane;
 
   float M = -INFINITY;
-  for (int c = lane; c < nck; c += 64) M = fmaxf(M, ml[2 * c]);
+  for (int c = lane; c < nck; c += 64) M = fmaxf(M, ml[c].x);
   // wave-wide maximum (order does not matter for max)
   M = fmaxf(M, __shfl_xor(M, 1));
   M = fmaxf(M, __shfl_xor(M, 2));
@@ -255,33 +266,52 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int c = 0; c < nck; ++c) {  // fixed chunk order
-    const float w = fast_exp2(ml[2 * c] - Ms);
-    L = __builtin_fmaf(w, ml[2 * c + 1], L);
+  // fixed chunk order; the loads of U chunks are in flight together
+  for (int c0 = 0; c0 < nck; c0 += U) {
+    float2 mlv[U];
+    vec pv[U];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const int d = lane + 64 * e;
-      if (d < D) o[e] = __builtin_fmaf(w, po[(size_t)c * D + d], o[e]);
+    for (int u = 0; u < U; ++u) {
+      const int c = min(c0 + u, nck - 1);
+      mlv[u] = ml[c];
+      pv[u] = po[(size_t)c * (D / DPL)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u < nck) {
+        const float w = fast_exp2(mlv[u].x - Ms);
+        L = __builtin_fmaf(w, mlv[u].y, L);
+        if constexpr (DPL == 2) {
+          o[0] = __builtin_fmaf(w, pv[u].x, o[0]);
+          o[1] = __builtin_fmaf(w, pv[u].y, o[1]);
+        } else {
+          o[0] = __builtin_fmaf(w, pv[u], o[0]);
+        }
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T* out = (T*)a.o + (size_t)bh * D;
+  T* out = (T*)a.o + (size_t)bh * D + lane * DPL;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    const int d = lane + 64 * e;
-    if (d < D) out[d] = (T)(o[e] * inv);
-  }
+  for (int e = 0; e < DPL; ++e) out[e] = (T)(o[e] * inv);
   if (lane == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
 }
 
-template <typename T, int D, int NW>
-static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
-  // enough workgroups to keep every CU busy; the loop covers the rest
-  const long long items = (long long)a.NC * a.B * a.H;
-  const long long cap = 256LL * 8;
-  const unsigned grid = (unsigned)(items < cap ? items : cap);
+#ifndef FA_DECODE_KPW
+#define FA_DECODE_KPW 64
+#endif
+
+template <typename T, int D, int CHUNK>
+static hipError_t launch_chunk(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int KPW = CHUNK < FA_DECODE_KPW ? CHUNK : FA_DECODE_KPW;  // keys per wave
+  constexpr int NW = CHUNK / KPW;
+  // One workgroup per work item: finished workgroups are replaced at once,
+  // so the load phase of some overlaps the arithmetic of others.  (A
+  // resident grid striding over the items runs its workgroups in step and
+  // was measured slower.)
+  const unsigned grid = (unsigned)((long long)a.NC * a.B * a.H);
   if (grid > 0)
-    hipLaunchKernelGGL((decode_partial_kernel<T, D, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, NW, KPW>), dim3(grid), dim3(NW * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, stream, a);
@@ -291,10 +321,10 @@ static hipError_t launch_nw(const DecodeArgs& a, hipStream_t stream) {
 template <typename T, int D>
 static hipError_t launch_td(const DecodeArgs& a, hipStream_t stream) {
   switch (a.chunk) {
-    case 64: return launch_nw<T, D, 1>(a, stream);
-    case 128: return launch_nw<T, D, 2>(a, stream);
-    case 256: return launch_nw<T, D, 4>(a, stream);
-    default: return launch_nw<T, D, 8>(a, stream);
+    case 64: return launch_chunk<T, D, 64>(a, stream);
+    case 128: return launch_chunk<T, D, 128>(a, stream);
+    case 256: return launch_chunk<T, D, 256>(a, stream);
+    default: return launch_chunk<T, D, 512>(a, stream);
   }
 }
 
