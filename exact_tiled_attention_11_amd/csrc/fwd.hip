@@ -114,6 +114,46 @@ __device__ __forceinline__ u32x4_t make_rsrc(const char* base, unsigned bytes) {
   return r;
 }
 
+// The (sequence, head, query block) a workgroup computes.  Fixed-length
+// grids take query blocks as levels with (batch, head) fastest, causal ones
+// longest first; varlen grids read the sorted tile list of the schedule
+// kernel and may hold more workgroups than tiles (then false).
+struct WorkItem {
+  int h, qblk, lq, lk;
+  long long q_tok0, k_tok0, lse_base;
+};
+template <bool CAUSAL, bool VARLEN>
+__device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
+  if constexpr (!VARLEN) {
+    const int nbh = a.B * a.H;
+    const int level = blockIdx.x / nbh;
+    const int bh = blockIdx.x - level * nbh;
+    w.qblk = CAUSAL ? (a.nqb - 1 - level) : level;
+    const int b = bh / a.H;
+    w.h = bh - b * a.H;
+    w.lq = a.Nq;
+    w.lk = a.Nk;
+    if (a.seqlens_k) w.lk = min(max(a.seqlens_k[b], 0), a.Nk);
+    w.q_tok0 = (long long)b * a.Nq;
+    w.k_tok0 = (long long)b * a.Nk;
+    w.lse_base = ((long long)b * a.H + w.h) * a.Nq;
+  } else {
+    const int t = blockIdx.x / a.H;
+    w.h = blockIdx.x - t * a.H;
+    if (t >= a.sched[0]) return false;
+    const int* tl = a.sched + 2 + 4 * a.nseq + 2 * t;
+    const int s = tl[0];
+    w.qblk = tl[1];
+    const int* sq = a.sched + 2 + 4 * s;
+    w.q_tok0 = sq[0];
+    w.lq = sq[1];
+    w.k_tok0 = sq[2];
+    w.lk = sq[3];
+    w.lse_base = (long long)w.h * a.total_q + w.q_tok0;
+  }
+  return true;
+}
+
 template <typename T, int D, int QB, int KB, int NW, int NBUF, int OCC, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   using C = FwdCfg<T, D, QB, KB, NW, NBUF>;
@@ -134,35 +174,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const int hh = lane >> 5;
 
   // ---- which (sequence, head, query block) this workgroup computes ----
-  int h, qblk, lq, lk;
-  long long q_tok0, k_tok0, lse_base;
-  if constexpr (!VARLEN) {
-    const int nbh = a.B * a.H;
-    const int level = blockIdx.x / nbh;
-    const int bh = blockIdx.x - level * nbh;
-    qblk = CAUSAL ? (a.nqb - 1 - level) : level;
-    const int b = bh / a.H;
-    h = bh - b * a.H;
-    lq = a.Nq;
-    lk = a.Nk;
-    if (a.seqlens_k) lk = min(max(a.seqlens_k[b], 0), a.Nk);
-    q_tok0 = (long long)b * a.Nq;
-    k_tok0 = (long long)b * a.Nk;
-    lse_base = ((long long)b * a.H + h) * a.Nq;
-  } else {
-    const int t = blockIdx.x / a.H;
-    h = blockIdx.x - t * a.H;
-    if (t >= a.sched[0]) return;  // whole workgroup leaves together
-    const int* tl = a.sched + 2 + 4 * a.nseq + 2 * t;
-    const int s = tl[0];
-    qblk = tl[1];
-    const int* sq = a.sched + 2 + 4 * s;
-    q_tok0 = sq[0];
-    lq = sq[1];
-    k_tok0 = sq[2];
-    lk = sq[3];
-    lse_base = (long long)h * a.total_q + q_tok0;
-  }
+  WorkItem wi;
+  if (!work_item<CAUSAL, VARLEN>(a, wi)) return;  // whole workgroup leaves together
+  const int h = wi.h, qblk = wi.qblk, lq = wi.lq, lk = wi.lk;
+  const long long q_tok0 = wi.q_tok0, k_tok0 = wi.k_tok0, lse_base = wi.lse_base;
 
   const int q0 = qblk * C::kBR;
   const int off = lk - lq;  // bottom-right causal alignment
@@ -487,6 +502,357 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined prefill for 16-bit types at head_dim 64.
+//
+// The three stages of a key block — scores S = K Q^T (MFMA), softmax
+// (VALU), P V (MFMA) — depend on each other only within the block, so while
+// a wave turns the scores of block u into probabilities, the MFMAs of P V
+// for block u-1 and of the scores of block u+1 are issued between its VALU
+// instructions.  A single wave cannot keep the VALU busy on its own, so the
+// register budget is held to four waves per SIMD: blocks of 32 keys, one
+// score set, one exponent set and one probability set per wave.
+//
+// LDS holds two rings of 32-key slots: K slots for blocks u+1 .. u+PK+1 and
+// V slots for blocks u-1 .. u+PK, so each block is requested PK steps
+// before its first use.  Every step issues exactly one K and one V load per
+// lane (past the last block the buffer range is empty and the load writes
+// zeros), which keeps the count of loads a step may leave pending constant;
+// the first of those zero loads fills the V slot of "block -1", whose
+// probabilities are zero too.
+// ---------------------------------------------------------------------------
+#ifndef FA_PIPE_LA
+#define FA_PIPE_LA 2  // LDS reads issued this many MFMAs ahead in the hot step
+#endif
+#ifndef FA_PIPE_PK
+#define FA_PIPE_PK 2  // steps between a block's request and its first use
+#endif
+
+template <typename T, int D, int NW, int PK>
+struct PipeCfg {
+  static constexpr int kBC = 32;                   // keys per block
+  static constexpr int kBR = NW * 32;              // query rows per workgroup
+  static constexpr int kNT = NW * 64;
+  static constexpr int kRowB = D * 2;              // bytes of one K or V row
+  static constexpr int kCPR = kRowB / 16;          // 16-byte chunks per row
+  static constexpr int kSlotB = kBC * kRowB;       // one K or V block
+  // Both rings have kNS slots (K needs PK+1, V needs PK+2), so slot offsets
+  // repeat every kNS steps and the step loop, unrolled by kNS, addresses LDS
+  // with constant offsets.
+  static constexpr int kNS = PK + 2;
+  static constexpr int kVBase = kNS * kSlotB;      // byte offset of the V ring
+  static constexpr int kLdsB = 2 * kNS * kSlotB;
+  static_assert(kBC * kCPR == 64 * NW, "one 16-byte load per lane per block");
+  static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
+  using C = PipeCfg<T, D, NW, PK>;
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  static_assert(E::kBytes == 2 && D == 64, "16-bit element types at head_dim 64");
+  constexpr int KS = D / E::kStep;  // MFMA steps over head_dim (4)
+  constexpr int DB = D / 32;        // 32-wide blocks of head_dim (2)
+  constexpr int TS = 32 / E::kStep; // MFMA steps over a 32-key block (2)
+  constexpr int RB = C::kCPR * 16;  // LDS bytes per block row
+  constexpr int LA = FA_PIPE_LA;
+
+  extern __shared__ __attribute__((aligned(16))) u32x4_t smem[];  // C::kLdsB bytes
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
+  const int col = lane & 31;
+  const int hh = lane >> 5;
+
+  WorkItem wi;
+  if (!work_item<CAUSAL, VARLEN>(a, wi)) return;  // whole workgroup leaves together
+  const int lq = wi.lq, lk = wi.lk;
+
+  const int q0 = wi.qblk * C::kBR;
+  const int off = lk - lq;  // bottom-right causal alignment
+  int nst = (lk + C::kBC - 1) / C::kBC;  // key blocks of the workgroup
+  if (CAUSAL) {
+    const int kmax = min(q0 + C::kBR, lq) - 1 + off;
+    nst = kmax < 0 ? 0 : min(nst, kmax / C::kBC + 1);
+  }
+  const int wq0 = q0 + wave * 32;
+  const int wq_last = min(wq0 + 32, lq) - 1;
+  int nw = 0;  // this wave's blocks: the prefix 0 .. nw-1
+  if (wq_last >= wq0) {
+    nw = nst;
+    if (CAUSAL) {
+      const int t = wq_last + off;
+      nw = t < 0 ? 0 : min(nst, t / C::kBC + 1);
+    }
+  }
+
+  const size_t rs = (size_t)a.H * D;  // elements between consecutive tokens
+  const T* qp = (const T*)a.q + (size_t)wi.q_tok0 * rs + (size_t)wi.h * D;
+  const char* kp = (const char*)((const T*)a.k + (size_t)wi.k_tok0 * rs + (size_t)wi.h * D);
+  const char* vp = (const char*)((const T*)a.v + (size_t)wi.k_tok0 * rs + (size_t)wi.h * D);
+  const unsigned rsb = (unsigned)(rs * sizeof(T));
+
+  // this lane's 16-byte chunk of a block: row r, LDS position pos
+  unsigned voff;
+  {
+    const int p = wave * 64 + lane;
+    const int r = p / C::kCPR, pos = p % C::kCPR;
+    voff = (unsigned)r * rsb + (unsigned)((pos ^ swz_f<C::kCPR, false>(r)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(size_t)(FA_LDS(char)*)smem;
+  // slot offsets of the block whose index is congruent to r modulo kNS
+  constexpr auto kslot = [](int r) { return ((r % C::kNS + C::kNS) % C::kNS) * C::kSlotB; };
+  constexpr auto vslot = [](int r) { return C::kVBase + ((r % C::kNS + C::kNS) % C::kNS) * C::kSlotB; };
+  // one block of K or V into its slot (an empty range past the last block)
+  auto load = [&](const char* base, int u, int slot) __attribute__((always_inline)) {
+    const int rows = (u >= 0 && u < nst) ? min(C::kBC, lk - u * C::kBC) : 0;
+    const u32x4_t rsrc = make_rsrc(base + (size_t)(u > 0 ? u : 0) * C::kBC * rsb, (unsigned)rows * rsb);
+    dma16(rsrc, voff, __builtin_amdgcn_readfirstlane(lds0 + slot + wave * 1024));
+  };
+  // step s (s = r mod kNS) requests K of block s+PK+1, then V of block s+PK
+  auto issue = [&](int s, auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    load(kp, s + PK + 1, kslot(r + PK + 1));
+    load(vp, s + PK, vslot(r + PK));
+  };
+
+  for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
+
+  frag qf[KS];
+  {
+    const int qi = wq0 + col;
+    const bool ok = qi < lq;
+    const T* row = qp + (size_t)(ok ? qi : 0) * rs;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      qf[ks] = ok ? *(const frag*)(row + ks * 16 + hh * 8) : z;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // Q complete before any block load is counted
+
+  f32x16_t oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+  float mrow = -INFINITY;  // running offset (units of scale*log2 e); -inf: no key yet
+  float lrow = 0.f;        // running sum over this lane's keys
+  __syncthreads();         // LDS zeroed before any block lands
+
+  int klane[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    klane[ks] = col * RB + ((ks * 2 + hh) ^ swz_f<C::kCPR, false>(col)) * 16;
+  int vlane[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    const int g = lane >> 4, ii = lane & 15, jj = ii >> 2, qq = ii & 3;
+    const int rr = 4 * hh + jj;
+    const int ch = 4 * i + 2 * (g & 1) + (qq >> 1);
+    vlane[i] = rr * RB + ((ch ^ swz_f<C::kCPR, false>(rr)) * 16) + (qq & 1) * 8;
+  }
+
+  // nw + 1, hidden from the optimizer: relating it to the loop bound makes
+  // the compiler restructure the loop in a way that doubles the registers
+  // the accumulators take
+  int nwp = nw + 1;
+  asm volatile("" : "+s"(nwp));
+  auto need_mask = [&](int u) __attribute__((always_inline)) {
+    const int k0 = u * C::kBC;
+    return (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > wq0 + off);
+  };
+
+  // Register roles (fixed, so nothing is copied between blocks):
+  //   sS  raw scores S^T of the next block to be exponentiated;
+  //   sX  exponents c*s - m of the current block (kept for a rescale);
+  //   pk  probabilities as P V operands: those of block u-1 until its P V
+  //       MFMAs have read them, then those of block u.
+  f32x16_t sS, sX;
+  frag pk[TS];
+#pragma unroll
+  for (int t = 0; t < TS; ++t) pk[t] = frag{};
+
+  // fragments of the block in slot r (a compile-time constant)
+  auto kfrag = [&](auto rc, int ks) __attribute__((always_inline)) -> frag {
+    constexpr int r = decltype(rc)::value;
+    return *(const frag*)((const char*)smem + kslot(r) + klane[ks]);
+  };
+  auto vfrag = [&](auto rc, int t, int db) __attribute__((always_inline)) -> frag {
+    constexpr int r = decltype(rc)::value;
+    const int base = vslot(r) + vlane[db] + 16 * t * RB;
+    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + base));
+    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + base + 8 * RB));
+    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+    const u32x4_t w = {lo2.x, lo2.y, hi2.x, hi2.y};
+    return __builtin_bit_cast(frag, w);
+  };
+  // S^T = K Q^T of block 0 into sS
+  auto scores0 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sS = mma(kfrag(IC<0>{}, ks), qf[ks], ks == 0 ? f32x16_t{} : sS);
+  };
+  // probabilities exp2(sX) into pk; returns this lane's sum
+  auto probs = [&]() __attribute__((always_inline)) -> float {
+    float ts = 0.f;
+#pragma unroll
+    for (int t = 0; t < TS; ++t) {
+      u32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = fast_exp2(sX[8 * t + 2 * e]);
+        const float p1 = fast_exp2(sX[8 * t + 2 * e + 1]);
+        ts += p0;
+        ts += p1;
+        w[e] = pack2(p0, p1, (T*)nullptr);
+      }
+      pk[t] = __builtin_bit_cast(frag, w);
+    }
+    return ts;
+  };
+  // lazy offset: raise m only if a probability could exceed 2^15 or the row
+  // has seen no key yet; then rescale O and l and redo the block
+  auto settle = [&](float ts) __attribute__((always_inline)) {
+    const bool need = (mrow == -INFINITY) || !(ts <= 0x1p15f);
+    if (__any(need)) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sX[r]);
+      const float mx = half_max(m);
+      const bool fresh = mrow == -INFINITY;
+      const bool none = !(mx > -1e30f);  // no visible key in this block
+      float delta;
+      if (fresh) delta = none ? 0.f : mx;
+      else delta = mx > kTau ? mx : 0.f;
+      const float mold = fresh ? 0.f : mrow;
+      const float alpha = fresh ? 0.f : fast_exp2(-delta);
+      mrow = (fresh && none) ? -INFINITY : mold + delta;
+      lrow *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sX[r] -= delta;
+      ts = probs();
+    }
+    lrow += ts;
+  };
+
+  // Block u.  First the exponents c*s - m of its scores (and, for a masked
+  // block, the mask: a hidden score becomes -2^109 or less; key 8*(r>>2) +
+  // 4*hh + (r&3) of the block is visible iff 8*(r>>2) + (r&3) <= lim, the
+  // bound added to each element's constant, which stays an instruction
+  // literal).  Then 8 chunks of one MFMA each (4 of P V for block u-1, then
+  // 4 of the scores of block u+1); chunk c also issues the LDS read of MFMA
+  // c+LA, takes exp2 of score pair c and adds and packs pair c-1, so the
+  // softmax's VALU work runs between MFMAs.  Scheduling fences keep the
+  // chunks in order.  One body serves masked and unmasked blocks: two
+  // copies of it would not fit the register budget.
+  auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    const float ms = mrow == -INFINITY ? 0.f : mrow;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sX[r] = __builtin_fmaf(sS[r], a.c, -ms);
+    if (masked) {
+      const int qi = wq0 + col;
+      const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;
+      const float base = (float)(last - u * C::kBC - 4 * hh) * 0x1p110f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float cr = (float)(8 * (r >> 2) + (r & 3));
+        sX[r] = fminf(sX[r], base + (0.5f - cr) * 0x1p110f);
+      }
+    }
+    frag op[8];  // LDS operand of MFMA i
+    auto read = [&](int i) __attribute__((always_inline)) {
+      if (i < 4) op[i] = vfrag(IC<(r + C::kNS - 1) % C::kNS>{}, i >> 1, i & 1);
+      else op[i] = kfrag(IC<(r + 1) % C::kNS>{}, i - 4);
+    };
+    auto mf = [&](int i) __attribute__((always_inline)) {
+      if (i < 4) oacc[i & 1] = mma(op[i], pk[i >> 1], oacc[i & 1]);
+      else sS = mma(op[i], qf[i - 4], i == 4 ? f32x16_t{} : sS);
+    };
+    float pe[16];
+    auto exp2c = [&](int c) __attribute__((always_inline)) {
+      pe[2 * c] = fast_exp2(sX[2 * c]);
+      pe[2 * c + 1] = fast_exp2(sX[2 * c + 1]);
+    };
+    float ts = 0.f;
+    auto acc2 = [&](int c) __attribute__((always_inline)) {
+      ts += pe[2 * c];
+      ts += pe[2 * c + 1];
+      u32x4_t w = __builtin_bit_cast(u32x4_t, pk[c >> 2]);
+      w[c & 3] = pack2(pe[2 * c], pe[2 * c + 1], (T*)nullptr);
+      pk[c >> 2] = __builtin_bit_cast(frag, w);
+    };
+#pragma unroll
+    for (int i = 0; i < LA; ++i) read(i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c + LA < 8) read(c + LA);
+      mf(c);
+      exp2c(c);
+      if (c >= 1) acc2(c - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    acc2(7);
+    settle(ts);
+  };
+
+  // Step u: blocks u+1 (K) and u-1 (V) must be in; then P V of u-1, scores
+  // of u+1 and the softmax of u.  The scores of u+1 on a wave's last block
+  // are computed and never used.
+  auto step = [&](int u, auto rc) __attribute__((always_inline)) {
+    vm_wait<2 * PK - 1>();  // later requests (V of u, and PK-1 steps' worth) may stay pending
+    __syncthreads();        // every wave's part is in; the slots of K u and V u-2 are free
+    issue(u, rc);
+    // At u = nw every key of the block is hidden from this wave's rows (it
+    // lies past the last one they see), so the masked form adds nothing but
+    // the last P V.
+    if (u < nwp) step_block(u, u == nw || need_mask(u), rc);
+  };
+
+  // requests of steps -PK-1 .. -1: K of blocks 0 .. PK, V of blocks -1 .. PK-1
+  [&]<int... S>(std::integer_sequence<int, S...>) {
+    (issue(S - PK - 1, IC<(S - PK - 1 + 4 * C::kNS) % C::kNS>{}), ...);
+  }(std::make_integer_sequence<int, PK + 1>{});
+  vm_wait<2 * PK + 1>();  // K of block 0 is in
+  __syncthreads();
+  if (nw > 0) scores0();
+  // steps 0 .. nst, unrolled by kNS so every slot offset is a constant (the
+  // steps past nst issue empty requests and compute nothing)
+  for (int u0 = 0; u0 <= nst; u0 += C::kNS) {
+    [&]<int... R>(std::integer_sequence<int, R...>) {
+      (step(u0 + R, IC<R>{}), ...);
+    }(std::make_integer_sequence<int, C::kNS>{});
+  }
+
+  // ---- epilogue: O = O / l, lse = m + log2 l (converted to natural log) ----
+  const float lt = half_sum(lrow);
+  const int qi = wq0 + col;
+  if (qi < lq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    T* orow = (T*)a.o + (size_t)(wi.q_tok0 + qi) * rs + (size_t)wi.h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * hh;
+        const float x0 = oacc[db][4 * g4 + 0] * inv, x1 = oacc[db][4 * g4 + 1] * inv;
+        const float x2 = oacc[db][4 * g4 + 2] * inv, x3 = oacc[db][4 * g4 + 3] * inv;
+        u32x2_t w = {pack2(x0, x1, (T*)nullptr), pack2(x2, x3, (T*)nullptr)};
+        *(u32x2_t*)(orow + d) = w;
+      }
+    if (hh == 0 && a.lse)
+      a.lse[wi.lse_base + qi] = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Varlen schedule: one workgroup sorts the (sequence, query block) tiles by
 // their number of key tiles, longest first (counting sort over LDS bins).
 // ---------------------------------------------------------------------------
@@ -606,9 +972,32 @@ static hipError_t launch_k(K kern, unsigned grid, int threads, int lds, hipStrea
   return hipGetLastError();
 }
 
+// 16-bit types at head_dim 64 take the software-pipelined kernel (same
+// 128-row blocks as Tile<., 64>; its 32-key blocks fit the 64-key tiles the
+// varlen schedule counts, which only needs an upper bound).
+#ifndef FA_PIPE
+#define FA_PIPE 1
+#endif
+template <typename T, int D>
+struct UsePipe {
+  static constexpr bool value = FA_PIPE && sizeof(T) == 2 && D == 64;
+};
+static_assert(Tile<__bf16, 64>::QB == 1 && Tile<__bf16, 64>::NW == 4,
+              "pipelined kernel rows per workgroup must match the dispatch tables");
+
 template <typename T, int D>
 static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned grid,
                            hipStream_t stream) {
+  if constexpr (UsePipe<T, D>::value) {
+    constexpr int NW = 4, PK = FA_PIPE_PK;
+    constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
+    if (causal) {
+      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false>, grid, NW * 64, lds, stream, a);
+    }
+    if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true>, grid, NW * 64, lds, stream, a);
+    return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false>, grid, NW * 64, lds, stream, a);
+  }
   using Tl = Tile<T, D>;
   constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;
   constexpr int lds = FwdCfg<T, D, QB, KB, NW, NB>::kLdsB;
