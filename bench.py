@@ -219,7 +219,7 @@ def main():
         out["unit"] = "TFLOP/s"
         out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                           "traffic": traffic, "kernel": "fwd_kernel<bf16,64,causal>",
+                           "traffic": traffic, "kernel": "fwd_pipe_kernel<bf16,64,causal>",
                            "ms_per_launch": pm, "ms_min": min(tp),
                            "algorithmic_flops_per_launch": pflops}
         cfg["workload"] = "prefill: %s" % wp.name
