@@ -33,7 +33,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (fp16 the same)
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["exact_tiled_attention_11_amd/csrc/fwd.hip",
                   "exact_tiled_attention_11_amd/csrc/decode.hip",
@@ -123,6 +124,60 @@ def cpu_baseline(w, budget_s=20.0):
     }
 
 
+def run_config(n, args, dev):
+    """Time the library call of one workload of the benchmark table alone
+    (the parity-test configurations) and print one JSON line for it."""
+    import torch
+    import workloads as wl
+    import exact_tiled_attention_11_amd as fa
+    w = wl.CFG[n]
+    log("generating inputs for %s" % w.name)
+    if w.kind == "prefill":
+        q, k, v = make_prefill(w, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        call = lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    elif w.kind == "varlen":
+        q, k, v, cu = wl.varlen_inputs(w)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        cud = torch.from_numpy(cu).to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_fwd_varlen_workspace_bytes(len(cu) - 1, q.shape[0]),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: fa.fwd_varlen(q, k, v, cud, cud, causal=w.causal, scale=w.scale, out=o,
+                                     lse=lse, workspace=ws)
+    else:
+        dq, kc, vc, sl = make_decode(w, dev)
+        o = torch.empty_like(dq)
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_decode_workspace_bytes(w.B, w.H, w.Nk, w.D, w.chunk),
+                         dtype=torch.uint8, device=dev)
+        call = lambda: fa.decode_splitkv(dq, kc, vc, sl, scale=w.scale, chunk=w.chunk, out=o,
+                                         lse=lse, workspace=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    ms, med = sum(t) / len(t), t[len(t) // 2]
+    if w.kind == "decode":
+        val, unit, peak, bound = w.bytes_moved() / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS, "hbm"
+    else:
+        peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        val, unit, bound = w.flops() / (ms * 1e-3) / 1e12, "TFLOP/s", "mfma"
+    print(json.dumps({"config": w.name, "kind": w.kind, "dtype": w.dtype, "value": val, "unit": unit,
+                      "ms_per_call": ms, "ms_median": med, "ms_min": t[0], "steps": args.steps,
+                      "roofline": {"bound": bound, "achieved": val, "peak": peak, "unit": unit,
+                                   "frac": val / peak}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +188,9 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
+    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5], default=None,
+                    help="time one workload of the benchmark table alone (its library call "
+                         "only) and print a JSON line for it instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "
@@ -146,6 +204,9 @@ def main():
     fa.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config is not None:
+        run_config(args.config, args, dev)
+        return
     if args.only == "copy":
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

@@ -502,15 +502,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined prefill for 16-bit types at head_dim 64.
+// Software-pipelined prefill for 16-bit types (head_dim 64 and 128).
 //
 // The three stages of a key block — scores S = K Q^T (MFMA), softmax
 // (VALU), P V (MFMA) — depend on each other only within the block, so while
 // a wave turns the scores of block u into probabilities, the MFMAs of P V
 // for block u-1 and of the scores of block u+1 are issued between its VALU
-// instructions.  A single wave cannot keep the VALU busy on its own, so the
-// register budget is held to four waves per SIMD: blocks of 32 keys, one
-// score set, one exponent set and one probability set per wave.
+// instructions.  Blocks are 32 keys, with one score set, one exponent set
+// and one probability set per wave, so head_dim 64 (VALU-bound: per score
+// the exponent, exp2, sum and pack outweigh the 4*64 MFMA flops) fits four
+// waves per SIMD; head_dim 128 (MFMA-bound) runs two.
 //
 // LDS holds two rings of 32-key slots: K slots for blocks u+1 .. u+PK+1 and
 // V slots for blocks u-1 .. u+PK, so each block is requested PK steps
@@ -541,7 +542,8 @@ struct PipeCfg {
   static constexpr int kNS = PK + 2;
   static constexpr int kVBase = kNS * kSlotB;      // byte offset of the V ring
   static constexpr int kLdsB = 2 * kNS * kSlotB;
-  static_assert(kBC * kCPR == 64 * NW, "one 16-byte load per lane per block");
+  static constexpr int kLPS = kBC * kCPR / (64 * NW);  // 16-byte loads per lane per block
+  static_assert(kBC * kCPR % (64 * NW) == 0, "a block divides evenly over the lanes");
   static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
 };
 
@@ -549,16 +551,22 @@ template <int N>
 using IC = std::integral_constant<int, N>;
 
 template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdArgs a) {
   using C = PipeCfg<T, D, NW, PK>;
   using E = Elem<T>;
   using frag = typename E::frag;
-  static_assert(E::kBytes == 2 && D == 64, "16-bit element types at head_dim 64");
-  constexpr int KS = D / E::kStep;  // MFMA steps over head_dim (4)
-  constexpr int DB = D / 32;        // 32-wide blocks of head_dim (2)
+  static_assert(E::kBytes == 2 && (D == 64 || D == 128), "16-bit element types, head_dim 64 or 128");
+  constexpr int KS = D / E::kStep;  // MFMA steps over head_dim (score MFMAs per block)
+  constexpr int DB = D / 32;        // 32-wide blocks of head_dim
   constexpr int TS = 32 / E::kStep; // MFMA steps over a 32-key block (2)
   constexpr int RB = C::kCPR * 16;  // LDS bytes per block row
   constexpr int LA = FA_PIPE_LA;
+  constexpr int LPS = C::kLPS;
+  constexpr int NPV = TS * DB;      // P V MFMAs per block
+  constexpr int NCH = NPV + KS;     // MFMAs (chunks) per block
+  constexpr int RP = NCH / 8;       // chunks per score pair
+  constexpr int ALAG = DB - 1;      // chunks from a pair's exp2 to its add and pack
+  static_assert(NCH % 8 == 0, "whole chunks per score pair");
 
   extern __shared__ __attribute__((aligned(16))) u32x4_t smem[];  // C::kLdsB bytes
 
@@ -597,11 +605,12 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
   const unsigned rsb = (unsigned)(rs * sizeof(T));
 
   // this lane's 16-byte chunk of a block: row r, LDS position pos
-  unsigned voff;
-  {
-    const int p = wave * 64 + lane;
+  unsigned voff[LPS];
+#pragma unroll
+  for (int l = 0; l < LPS; ++l) {
+    const int p = (l * NW + wave) * 64 + lane;
     const int r = p / C::kCPR, pos = p % C::kCPR;
-    voff = (unsigned)r * rsb + (unsigned)((pos ^ swz_f<C::kCPR, false>(r)) * 16);
+    voff[l] = (unsigned)r * rsb + (unsigned)((pos ^ swz_f<C::kCPR, false>(r)) * 16);
   }
   const unsigned lds0 = (unsigned)(size_t)(FA_LDS(char)*)smem;
   // slot offsets of the block whose index is congruent to r modulo kNS
@@ -611,7 +620,9 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
   auto load = [&](const char* base, int u, int slot) __attribute__((always_inline)) {
     const int rows = (u >= 0 && u < nst) ? min(C::kBC, lk - u * C::kBC) : 0;
     const u32x4_t rsrc = make_rsrc(base + (size_t)(u > 0 ? u : 0) * C::kBC * rsb, (unsigned)rows * rsb);
-    dma16(rsrc, voff, __builtin_amdgcn_readfirstlane(lds0 + slot + wave * 1024));
+#pragma unroll
+    for (int l = 0; l < LPS; ++l)
+      dma16(rsrc, voff[l], __builtin_amdgcn_readfirstlane(lds0 + slot + (l * NW + wave) * 1024));
   };
   // step s (s = r mod kNS) requests K of block s+PK+1, then V of block s+PK
   auto issue = [&](int s, auto rc) __attribute__((always_inline)) {
@@ -746,10 +757,10 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
   // block, the mask: a hidden score becomes -2^109 or less; key 8*(r>>2) +
   // 4*hh + (r&3) of the block is visible iff 8*(r>>2) + (r&3) <= lim, the
   // bound added to each element's constant, which stays an instruction
-  // literal).  Then 8 chunks of one MFMA each (4 of P V for block u-1, then
-  // 4 of the scores of block u+1); chunk c also issues the LDS read of MFMA
-  // c+LA, takes exp2 of score pair c and adds and packs pair c-1, so the
-  // softmax's VALU work runs between MFMAs.  Scheduling fences keep the
+  // literal).  Then one chunk per MFMA (P V for block u-1, then the scores
+  // of block u+1); a chunk also issues the LDS read of a later MFMA and
+  // takes its share of the exp2, add and pack work of the score pairs, so
+  // the softmax's VALU work runs between MFMAs.  Scheduling fences keep the
   // chunks in order.  One body serves masked and unmasked blocks: two
   // copies of it would not fit the register budget.
   auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
@@ -767,14 +778,14 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
         sX[r] = fminf(sX[r], base + (0.5f - cr) * 0x1p110f);
       }
     }
-    frag op[8];  // LDS operand of MFMA i
+    frag op[NCH];  // LDS operand of MFMA i: P V (t-major) first, then the scores
     auto read = [&](int i) __attribute__((always_inline)) {
-      if (i < 4) op[i] = vfrag(IC<(r + C::kNS - 1) % C::kNS>{}, i >> 1, i & 1);
-      else op[i] = kfrag(IC<(r + 1) % C::kNS>{}, i - 4);
+      if (i < NPV) op[i] = vfrag(IC<(r + C::kNS - 1) % C::kNS>{}, i / DB, i % DB);
+      else op[i] = kfrag(IC<(r + 1) % C::kNS>{}, i - NPV);
     };
     auto mf = [&](int i) __attribute__((always_inline)) {
-      if (i < 4) oacc[i & 1] = mma(op[i], pk[i >> 1], oacc[i & 1]);
-      else sS = mma(op[i], qf[i - 4], i == 4 ? f32x16_t{} : sS);
+      if (i < NPV) oacc[i % DB] = mma(op[i], pk[i / DB], oacc[i % DB]);
+      else sS = mma(op[i], qf[i - NPV], i == NPV ? f32x16_t{} : sS);
     };
     float pe[16];
     auto exp2c = [&](int c) __attribute__((always_inline)) {
@@ -789,17 +800,22 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
       w[c & 3] = pack2(pe[2 * c], pe[2 * c + 1], (T*)nullptr);
       pk[c >> 2] = __builtin_bit_cast(frag, w);
     };
+    // pair p: exp2 in chunk p*RP, add and pack in chunk p*RP + ALAG; the
+    // probabilities of block u-1 in pk[t] are read by the P V MFMAs of
+    // chunks t*DB .. t*DB+DB-1, never after their replacement is written
 #pragma unroll
     for (int i = 0; i < LA; ++i) read(i);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (c + LA < 8) read(c + LA);
+    for (int c = 0; c < NCH; ++c) {
+      if (c + LA < NCH) read(c + LA);
       mf(c);
-      exp2c(c);
-      if (c >= 1) acc2(c - 1);
+      if (c % RP == 0) exp2c(c / RP);
+      if (c >= ALAG && (c - ALAG) % RP == 0) acc2((c - ALAG) / RP);
       __builtin_amdgcn_sched_barrier(0);
     }
-    acc2(7);
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      if (p * RP + ALAG >= NCH) acc2(p);
     settle(ts);
   };
 
@@ -807,7 +823,7 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
   // of u+1 and the softmax of u.  The scores of u+1 on a wave's last block
   // are computed and never used.
   auto step = [&](int u, auto rc) __attribute__((always_inline)) {
-    vm_wait<2 * PK - 1>();  // later requests (V of u, and PK-1 steps' worth) may stay pending
+    vm_wait<(2 * PK - 1) * LPS>();  // later requests (V of u, and PK-1 steps' worth) may stay pending
     __syncthreads();        // every wave's part is in; the slots of K u and V u-2 are free
     issue(u, rc);
     // At u = nw every key of the block is hidden from this wave's rows (it
@@ -820,7 +836,7 @@ __global__ __launch_bounds__(NW * 64, 4) void fwd_pipe_kernel(FwdArgs a) {
   [&]<int... S>(std::integer_sequence<int, S...>) {
     (issue(S - PK - 1, IC<(S - PK - 1 + 4 * C::kNS) % C::kNS>{}), ...);
   }(std::make_integer_sequence<int, PK + 1>{});
-  vm_wait<2 * PK + 1>();  // K of block 0 is in
+  vm_wait<(2 * PK + 1) * LPS>();  // K of block 0 is in
   __syncthreads();
   if (nw > 0) scores0();
   // steps 0 .. nst, unrolled by kNS so every slot offset is a constant (the
@@ -972,17 +988,18 @@ static hipError_t launch_k(K kern, unsigned grid, int threads, int lds, hipStrea
   return hipGetLastError();
 }
 
-// 16-bit types at head_dim 64 take the software-pipelined kernel (same
-// 128-row blocks as Tile<., 64>; its 32-key blocks fit the 64-key tiles the
-// varlen schedule counts, which only needs an upper bound).
+// 16-bit types take the software-pipelined kernel (same 128-row blocks as
+// Tile<., D>; its 32-key blocks fit the 64-key tiles the varlen schedule
+// counts, which only needs an upper bound).
 #ifndef FA_PIPE
 #define FA_PIPE 1
 #endif
 template <typename T, int D>
 struct UsePipe {
-  static constexpr bool value = FA_PIPE && sizeof(T) == 2 && D == 64;
+  static constexpr bool value = FA_PIPE && sizeof(T) == 2;
 };
-static_assert(Tile<__bf16, 64>::QB == 1 && Tile<__bf16, 64>::NW == 4,
+static_assert(Tile<__bf16, 64>::QB == 1 && Tile<__bf16, 64>::NW == 4 &&
+              Tile<__bf16, 128>::QB == 1 && Tile<__bf16, 128>::NW == 4,
               "pipelined kernel rows per workgroup must match the dispatch tables");
 
 template <typename T, int D>
