@@ -147,6 +147,24 @@ def run_config(n, args, dev):
                          dtype=torch.uint8, device=dev)
         call = lambda: fa.fwd_varlen(q, k, v, cud, cud, causal=w.causal, scale=w.scale, out=o,
                                      lse=lse, workspace=ws)
+    elif w.kind == "paged":
+        dq, kc, vc, sl = make_decode(w, dev)
+        table, num_pages = wl.page_layout(w, w.page_size)
+        bt = torch.from_numpy(table).to(dev)
+        pool = (num_pages, w.page_size, w.H, w.D)
+        idx = bt.flatten().long()
+        kp = torch.empty(pool, dtype=kc.dtype, device=dev)
+        kp[idx] = kc.view(-1, *pool[1:])
+        del kc
+        vp = torch.empty(pool, dtype=vc.dtype, device=dev)
+        vp[idx] = vc.view(-1, *pool[1:])
+        del vc
+        o = torch.empty_like(dq)
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(fa.fa_decode_workspace_bytes(w.B, w.H, table.shape[1] * w.page_size, w.D,
+                                                      w.chunk), dtype=torch.uint8, device=dev)
+        call = lambda: fa.decode_splitkv_paged(dq, kp, vp, sl, bt, scale=w.scale, chunk=w.chunk,
+                                               out=o, lse=lse, workspace=ws)
     else:
         dq, kc, vc, sl = make_decode(w, dev)
         o = torch.empty_like(dq)
@@ -167,7 +185,7 @@ def run_config(n, args, dev):
     torch.cuda.synchronize()
     t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     ms, med = sum(t) / len(t), t[len(t) // 2]
-    if w.kind == "decode":
+    if w.kind in ("decode", "paged"):
         val, unit, peak, bound = w.bytes_moved() / (ms * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS, "hbm"
     else:
         peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
@@ -188,9 +206,10 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
-    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5], default=None,
-                    help="time one workload of the benchmark table alone (its library call "
-                         "only) and print a JSON line for it instead of the bench line")
+    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5, 6], default=None,
+                    help="time one workload alone (its library call only) and print a JSON "
+                         "line for it instead of the bench line: 1-5 the benchmark table, "
+                         "6 its decode over a paged cache")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "

@@ -27,8 +27,8 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
     "fa_fwd", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
-    "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
-    "fwd", "fwd_varlen", "decode_splitkv",
+    "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
+    "fwd", "fwd_varlen", "decode_splitkv", "decode_splitkv_paged",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -46,6 +46,8 @@ _SIGS = {
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "fa_decode_splitkv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _sz,
                                _i, _vp]),
+    "fa_decode_splitkv_paged": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                     _f, _i, _vp, _sz, _i, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_i]),
     "fa_version": (ctypes.c_char_p, []),
 }
@@ -107,6 +109,14 @@ def fa_decode_splitkv(q, k_cache, v_cache, o, lse, seqlens_k, B, H, Nk_max, D, s
                       workspace, workspace_bytes, dtype, stream) -> int:
     return load().fa_decode_splitkv(q, k_cache, v_cache, o, lse, seqlens_k, B, H, Nk_max, D,
                                     scale, chunk, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_decode_splitkv_paged(q, k_pages, v_pages, o, lse, seqlens_k, block_table, B, H, num_pages,
+                            page_size, max_pages, D, scale, chunk, workspace, workspace_bytes,
+                            dtype, stream) -> int:
+    return load().fa_decode_splitkv_paged(q, k_pages, v_pages, o, lse, seqlens_k, block_table, B,
+                                          H, num_pages, page_size, max_pages, D, scale, chunk,
+                                          workspace, workspace_bytes, dtype, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -220,4 +230,30 @@ def decode_splitkv(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = N
                            _ptr(seqlens_k), B, H, Nk_max, D, float(scale), chunk,
                            _ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
     _check("fa_decode_splitkv", st)
+    return out, lse
+
+
+def decode_splitkv_paged(q, k_pages, v_pages, seqlens_k, block_table, *,
+                         scale: Optional[float] = None, chunk: int = 256, out=None, lse=None,
+                         return_lse: bool = True, workspace=None, stream=None) -> Tuple:
+    """Split-KV decode over a paged cache. q [B, H, D]; pages [num_pages, page_size, H, D];
+    block_table int32 [B, max_pages] -> (o [B, H, D], lse [B, H])."""
+    import torch
+    B, H, D = q.shape
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = fa_decode_workspace_bytes(B, H, max_pages * page_size, D, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = fa_decode_splitkv_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse),
+                                 _ptr(seqlens_k), _ptr(block_table), B, H, num_pages, page_size,
+                                 max_pages, D, float(scale), chunk, _ptr(workspace),
+                                 workspace.numel(), _dtype_code(q), _stream(stream))
+    _check("fa_decode_splitkv_paged", st)
     return out, lse

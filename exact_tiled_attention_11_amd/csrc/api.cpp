@@ -171,15 +171,17 @@ size_t fa_decode_workspace_bytes(int B, int H, int Nk_max, int D, int chunk) {
   return o_bytes + ml_bytes;
 }
 
-fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
-                              float* lse, const int32_t* seqlens_k, int B, int H, int Nk_max,
-                              int D, float scale, int chunk, void* workspace,
-                              size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+// Shared by the contiguous and the paged decode entry points; `a` carries the
+// cache pointers and, for a paged cache, the page table fields.
+static fa_status_t decode_common(fa::DecodeArgs& a, const void* q, void* o, float* lse,
+                                 const int32_t* seqlens_k, int B, int H, int Nk_max, int D,
+                                 float scale, int chunk, void* workspace,
+                                 size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128) || !chunk_ok(chunk)) return FA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || Nk_max < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-  if (!q || !o || !seqlens_k || ((!k_cache || !v_cache) && Nk_max > 0)) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+  if (!q || !o || !seqlens_k || ((!a.kc || !a.vc) && Nk_max > 0)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(a.kc) || !aligned16(a.vc) || !aligned16(o) ||
       !aligned16(lse) || !aligned16(workspace))
     return FA_ERR_INVALID_ARG;
   if ((long long)B * H * (((long long)Nk_max + chunk - 1) / chunk + 1) > 0x7fffffffLL)
@@ -192,10 +194,7 @@ fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_
 
   const int nc = (Nk_max + chunk - 1) / chunk;
   const size_t recs = (size_t)B * H * (nc > 0 ? nc : 1);
-  fa::DecodeArgs a = {};
   a.q = q;
-  a.kc = k_cache;
-  a.vc = v_cache;
   a.o = o;
   a.lse = lse;
   a.seqlens_k = seqlens_k;
@@ -208,6 +207,44 @@ fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_
   a.chunk = chunk;
   a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
   return from_hip(fa::launch_decode(a, dtype, D, (hipStream_t)stream));
+}
+
+fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, const void* v_cache, void* o,
+                              float* lse, const int32_t* seqlens_k, int B, int H, int Nk_max,
+                              int D, float scale, int chunk, void* workspace,
+                              size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  fa::DecodeArgs a = {};
+  a.kc = k_cache;
+  a.vc = v_cache;
+  return decode_common(a, q, o, lse, seqlens_k, B, H, Nk_max, D, scale, chunk, workspace,
+                       workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_decode_splitkv_paged(const void* q, const void* k_pages, const void* v_pages,
+                                    void* o, float* lse, const int32_t* seqlens_k,
+                                    const int32_t* block_table, int B, int H, int num_pages,
+                                    int page_size, int max_pages, int D, float scale, int chunk,
+                                    void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                                    void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128) || !chunk_ok(chunk)) return FA_ERR_UNSUPPORTED;
+  if (page_size < 16 || page_size > 1024 || (page_size & (page_size - 1)) != 0)
+    return FA_ERR_UNSUPPORTED;
+  if (num_pages < 1 || max_pages < 0) return FA_ERR_INVALID_ARG;
+  if (!block_table || ((uintptr_t)block_table & 3u) != 0) return FA_ERR_INVALID_ARG;
+  const long long nk = (long long)max_pages * page_size;
+  if (nk > 0x7fffffffLL || (long long)num_pages * page_size > 0x7fffffffLL)
+    return FA_ERR_INVALID_ARG;
+  fa::DecodeArgs a = {};
+  a.kc = k_pages;
+  a.vc = v_pages;
+  a.block_table = block_table;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages;
+  a.page_shift = 0;
+  while ((1 << a.page_shift) < page_size) ++a.page_shift;
+  if (!k_pages || !v_pages) return FA_ERR_INVALID_ARG;
+  return decode_common(a, q, o, lse, seqlens_k, B, H, (int)nk, D, scale, chunk, workspace,
+                       workspace_bytes, dtype, stream);
 }
 
 }  // extern "C"

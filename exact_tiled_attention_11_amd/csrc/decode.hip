@@ -105,8 +105,10 @@ __device__ __forceinline__ u32x4_t stream_load(const u32x4_t* p) {
   return __builtin_nontemporal_load(p);
 }
 
-// NW waves of KPW keys each cover one chunk of NW*KPW keys.
-template <typename T, int D, int NW, int KPW>
+// NW waves of KPW keys each cover one chunk of NW*KPW keys.  PAGED: the
+// cache is a pool of pages of 2^page_shift rows and block_table maps a batch
+// entry's key t to row t mod 2^page_shift of page block_table[b][t >> shift].
+template <typename T, int D, int NW, int KPW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeArgs a) {
   constexpr int ES = Elem<T>::kBytes;
   constexpr int EPL = 16 / ES;          // elements per 16-byte slice
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kk = lane / LPK;            // key slot within a wave-wide load
   const int dd = lane % LPK;            // 16-byte slice of the row
 
@@ -137,15 +139,29 @@ __global__ __launch_bounds__(NW * 64) void decode_partial_kernel(DecodeArgs a) {
     if (c * a.chunk >= lk) return;      // uniform over the workgroup
 
     const int key0 = c * a.chunk + wave * KPW;
-    const char* kb = (const char*)((const T*)a.kc + (size_t)b * a.Nk_max * rs + (size_t)h * D) + dd * 16;
-    const char* vb = (const char*)((const T*)a.vc + (size_t)b * a.Nk_max * rs + (size_t)h * D) + dd * 16;
+    // first row of this batch entry's cache (the page pool for a paged cache)
+    const size_t row0 = PAGED ? 0 : (size_t)b * a.Nk_max;
+    const char* kb = (const char*)((const T*)a.kc + row0 * rs + (size_t)h * D) + dd * 16;
+    const char* vb = (const char*)((const T*)a.vc + row0 * rs + (size_t)h * D) + dd * 16;
     u32x4_t kr[NI], vr[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int key = key0 + i * KPI + kk;
+      size_t row = (size_t)key;
+      if constexpr (PAGED) {
+        // The KPI keys of one load lie in one aligned group of at most 8 and
+        // pages hold at least 16 rows, so the page is the same for the whole
+        // wave: one scalar load, only for groups inside the sequence.  An id
+        // outside the pool is clamped into it (no read leaves the cache).
+        const int kbase = key0 + i * KPI;
+        int pg = 0;
+        if (kbase < lk) pg = a.block_table[(size_t)b * a.max_pages + (kbase >> a.page_shift)];
+        pg = min(max(pg, 0), a.num_pages - 1);
+        row = ((size_t)pg << a.page_shift) + (size_t)(key & ((1 << a.page_shift) - 1));
+      }
       if (key < lk) {
-        kr[i] = stream_load((const u32x4_t*)(kb + (size_t)key * rs * ES));
-        vr[i] = stream_load((const u32x4_t*)(vb + (size_t)key * rs * ES));
+        kr[i] = stream_load((const u32x4_t*)(kb + row * rs * ES));
+        vr[i] = stream_load((const u32x4_t*)(vb + row * rs * ES));
       } else {
         kr[i] = u32x4_t{};
         vr[i] = u32x4_t{};
@@ -301,7 +317,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
 #define FA_DECODE_KPW 64
 #endif
 
-template <typename T, int D, int CHUNK>
+template <typename T, int D, int CHUNK, bool PAGED>
 static hipError_t launch_chunk(const DecodeArgs& a, hipStream_t stream) {
   constexpr int KPW = CHUNK < FA_DECODE_KPW ? CHUNK : FA_DECODE_KPW;  // keys per wave
   constexpr int NW = CHUNK / KPW;
@@ -311,21 +327,26 @@ static hipError_t launch_chunk(const DecodeArgs& a, hipStream_t stream) {
   // was measured slower.)
   const unsigned grid = (unsigned)((long long)a.NC * a.B * a.H);
   if (grid > 0)
-    hipLaunchKernelGGL((decode_partial_kernel<T, D, NW, KPW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<T, D, NW, KPW, PAGED>), dim3(grid), dim3(NW * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
+template <typename T, int D, bool PAGED>
+static hipError_t launch_tdp(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.chunk) {
+    case 64: return launch_chunk<T, D, 64, PAGED>(a, stream);
+    case 128: return launch_chunk<T, D, 128, PAGED>(a, stream);
+    case 256: return launch_chunk<T, D, 256, PAGED>(a, stream);
+    default: return launch_chunk<T, D, 512, PAGED>(a, stream);
+  }
+}
+
 template <typename T, int D>
 static hipError_t launch_td(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.chunk) {
-    case 64: return launch_chunk<T, D, 64>(a, stream);
-    case 128: return launch_chunk<T, D, 128>(a, stream);
-    case 256: return launch_chunk<T, D, 256>(a, stream);
-    default: return launch_chunk<T, D, 512>(a, stream);
-  }
+  return a.block_table ? launch_tdp<T, D, true>(a, stream) : launch_tdp<T, D, false>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, fa_dtype_t dtype, int D, hipStream_t stream) {

@@ -66,6 +66,9 @@ struct DecodeArgs {
   float* ws_ml;    // [B, H, NC, 2]
   int B, H, Nk_max, NC, chunk;
   float c;
+  // paged cache (block_table == nullptr: contiguous [B, Nk_max, H, D] caches)
+  const int32_t* block_table;  // [B, max_pages]
+  int page_shift, num_pages, max_pages;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, fa_dtype_t dtype, int D, hipStream_t stream);

@@ -125,6 +125,33 @@ FA355_API fa_status_t fa_decode_splitkv(const void* q, const void* k_cache, cons
                               void* workspace, size_t workspace_bytes,
                               fa_dtype_t dtype, void* stream);
 
+/*
+ * The same split-KV decode over a paged cache: the keys and values of all
+ * batch entries live in one pool of fixed-size pages and a page table names
+ * each entry's pages in key order (the cache-layout question of the
+ * slavadubrov.com page's checklist, row on head dimension, mask and cache
+ * layout; the computation is the decode above on the gathered cache).
+ *   k_pages, v_pages: [num_pages, page_size, H, D]; key t of batch entry b is
+ *       row t % page_size of page block_table[b * max_pages + t / page_size]
+ *   block_table: device int32 [B, max_pages], 4-byte aligned; only the first
+ *       ceil(Lk / page_size) entries of a row are read; an entry outside
+ *       [0, num_pages) is a caller error: it is clamped into the pool (no read
+ *       leaves the cache) and that entry's output is unspecified
+ *   page_size: power of two, 16 .. 1024 (else FA_ERR_UNSUPPORTED)
+ *   Lk = min(max(seqlens_k[b], 0), max_pages * page_size)
+ *   workspace: at least fa_decode_workspace_bytes(B, H, max_pages * page_size,
+ *       D, chunk) bytes
+ * Other arguments, errors and ordering as fa_decode_splitkv; the caller owns
+ * every buffer.  Bit-identical to fa_decode_splitkv on the gathered cache.
+ */
+FA355_API fa_status_t fa_decode_splitkv_paged(const void* q, const void* k_pages,
+                              const void* v_pages, void* o, float* lse,
+                              const int32_t* seqlens_k, const int32_t* block_table,
+                              int B, int H, int num_pages, int page_size, int max_pages,
+                              int D, float scale, int chunk,
+                              void* workspace, size_t workspace_bytes,
+                              fa_dtype_t dtype, void* stream);
+
 /* Static strings; never NULL. */
 FA355_API const char* fa_status_string(fa_status_t status);
 FA355_API const char* fa_version(void);

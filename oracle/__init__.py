@@ -18,6 +18,7 @@ from .exact import (  # noqa: F401
     attention,
     attention_varlen,
     decode,
+    decode_paged,
     partial,
     merge,
     finalize,

@@ -186,6 +186,34 @@ def decode(q, k_cache, v_cache, seqlens_k, scale):
     return o, lse
 
 
+def decode_paged(q, k_pages, v_pages, block_table, seqlens_k, scale):
+    """Single-token decode over a paged cache (the slavadubrov.com page's
+    checklist row on head dimension, mask and cache layout: the layout of the
+    cache changes where keys are stored, not what is computed).
+
+    k_pages, v_pages: [num_pages, page_size, H, D]; key t of batch entry b is
+    row t % page_size of page block_table[b][t // page_size].  Each entry's
+    keys are gathered in key order and the decode definition is applied.
+    Returns O [B, H, D], lse [B, H].
+    """
+    q = np.asarray(q)
+    B, H, D = q.shape
+    page_size = k_pages.shape[1]
+    o = np.zeros((B, H, v_pages.shape[-1]), _F64)
+    lse = np.zeros((B, H), _F64)
+    for b in range(B):
+        lk = int(seqlens_k[b])
+        rows = [(int(block_table[b][t // page_size]), t % page_size) for t in range(lk)]
+        kb = np.array([k_pages[p, r] for p, r in rows], _F64).reshape(lk, H, k_pages.shape[-1])
+        vb = np.array([v_pages[p, r] for p, r in rows], _F64).reshape(lk, H, v_pages.shape[-1])
+        for h in range(H):
+            ob, lb = attention_rows(q[b, h][None, :], [0], kb[:, h, :], vb[:, h, :], 1, lk,
+                                    scale, False)
+            o[b, h] = ob[0]
+            lse[b, h] = lb[0]
+    return o, lse
+
+
 # ----------------------------------------------------------------------------
 # The tiled-softmax summary of the pages, kept separate from the definition
 # above so that tests can check one against the other.

@@ -27,7 +27,8 @@ def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
         "fa_fwd", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
-        "fa_decode_workspace_bytes", "fa_status_string", "fa_version"])
+        "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
+        "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -121,6 +122,35 @@ def test_decode_validation():
     assert call(wsb=100) == fa.FA_ERR_WORKSPACE
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(o=MIS) == fa.FA_ERR_INVALID_ARG
+
+
+def test_decode_paged_validation():
+    """Every argument check runs before any HIP call, so these need no GPU."""
+    base = dict(q=P, kc=P, vc=P, o=P, lse=P, sl=P, bt=P, B=2, H=2, npg=64, ps=16, mp=32, D=128,
+                scale=0.1, chunk=256, ws=P, wsb=1 << 20, dtype=fa.FA_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_decode_splitkv_paged(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["sl"],
+                                          a["bt"], a["B"], a["H"], a["npg"], a["ps"], a["mp"],
+                                          a["D"], a["scale"], a["chunk"], a["ws"], a["wsb"],
+                                          a["dtype"], a["stream"])
+    assert call(ps=24) == fa.FA_ERR_UNSUPPORTED          # not a power of two
+    assert call(ps=8) == fa.FA_ERR_UNSUPPORTED           # below 16 rows
+    assert call(ps=2048) == fa.FA_ERR_UNSUPPORTED
+    assert call(chunk=100) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(bt=None) == fa.FA_ERR_INVALID_ARG
+    assert call(bt=P + 2) == fa.FA_ERR_INVALID_ARG       # int32 table not 4-byte aligned
+    assert call(npg=0) == fa.FA_ERR_INVALID_ARG
+    assert call(mp=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(mp=1 << 27, ps=1024) == fa.FA_ERR_INVALID_ARG  # keys per entry overflow int32
+    assert call(kc=None) == fa.FA_ERR_INVALID_ARG
+    assert call(sl=None) == fa.FA_ERR_INVALID_ARG
+    assert call(wsb=100) == fa.FA_ERR_WORKSPACE
+    need = fa.fa_decode_workspace_bytes(2, 2, 32 * 16, 128, 256)
+    assert call(wsb=need - 1) == fa.FA_ERR_WORKSPACE
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):

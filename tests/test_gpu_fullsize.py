@@ -127,3 +127,50 @@ def test_decode_full_size_sampled():
                                                    L, w.scale, False)
             assert_close(w.dtype, wl.to_f64(o_c[b, h])[None], o_ref, lse_c[b, h:h + 1].double().numpy(),
                          lse_ref, "%s b%d h%d" % (w.name, b, h))
+
+
+def test_decode_paged_full_size_sampled():
+    """The decode workload over 16-row pages at shuffled pool positions, in the
+    launch configuration bench.py --config 6 times: bit-identical to the
+    contiguous call, and sampled (batch, head) rows against the oracle."""
+    fa = _fa()
+    w = wl.CFG[6]
+    lens = w.lengths()
+    say("generate %s" % w.name)
+    q = wl.decode_query(w)
+    kc = torch.empty((w.B, w.Nk, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    for b in range(w.B):
+        L = int(lens[b])
+        kc[b, :L].copy_(wl.decode_cache_rows(w, 1, b, L))
+        vc[b, :L].copy_(wl.decode_cache_rows(w, 2, b, L))
+        kc[b, L:min(w.Nk, L + 300)] = float("nan")
+        vc[b, L:min(w.Nk, L + 300)] = float("nan")
+    table, num_pages = wl.page_layout(w, w.page_size)
+    bt = torch.from_numpy(table).cuda()
+    pool = (num_pages, w.page_size, w.H, w.D)
+    kp = torch.full(pool, float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    kp[bt.flatten().long()] = kc.view(-1, *pool[1:])
+    vp[bt.flatten().long()] = vc.view(-1, *pool[1:])
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    say("fa_decode_splitkv_paged %s" % w.name)
+    o, lse = fa.decode_splitkv_paged(q.cuda(), kp, vp, sl, bt, scale=w.scale, chunk=w.chunk)
+    say("fa_decode_splitkv (contiguous) %s" % w.name)
+    oc, lc = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), oc.view(torch.int16)), "paged differs from contiguous"
+    assert torch.equal(lse.view(torch.int32), lc.view(torch.int32))
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    del kc, vc, kp, vp
+    rng = np.random.default_rng(1006)
+    for b in sorted({0, w.B - 1} | {int(x) for x in rng.integers(0, w.B, 3)}):
+        L = int(lens[b])
+        kb = wl.to_f64(wl.decode_cache_rows(w, 1, b, L))
+        vb = wl.to_f64(wl.decode_cache_rows(w, 2, b, L))
+        for h in sorted({0, int(rng.integers(w.H))}):
+            o_ref, lse_ref = oracle.attention_rows(wl.to_f64(q[b, h])[None], [0], kb[:, h], vb[:, h], 1,
+                                                   L, w.scale, False)
+            assert_close(w.dtype, wl.to_f64(o_c[b, h])[None], o_ref, lse_c[b, h:h + 1].double().numpy(),
+                         lse_ref, "%s b%d h%d" % (w.name, b, h))

@@ -184,3 +184,51 @@ DECODE = [
 @pytest.mark.parametrize("w", DECODE, ids=lambda w: w.name)
 def test_decode_cases(w):
     decode_case(w)
+
+
+def decode_paged_case(w, page_size, chunk=256):
+    """Paged cache at shuffled pool positions with NaN in every unused page
+    and row: against the oracle, and bit-identical to the contiguous call."""
+    fa = _fa()
+    q, kc, vc, lens = wl.decode_inputs_cpu(w)
+    table, num_pages = wl.page_layout(w, page_size)
+    kp, vp = wl.paged_from_cache(kc, vc, lens, table, num_pages, page_size)
+    qd, kpd, vpd = q.cuda(), kp.cuda(), vp.cuda()
+    sl, bt = torch.from_numpy(lens).cuda(), torch.from_numpy(table).cuda()
+    outs = []
+    for rep in range(2):
+        o = torch.full_like(qd, float("nan"))
+        lse = torch.full((w.B, w.H), float("nan"), dtype=torch.float32, device="cuda")
+        say("  fa_decode_splitkv_paged %s page %d chunk %d rep %d" % (w.name, page_size, chunk, rep))
+        fa.decode_splitkv_paged(qd, kpd, vpd, sl, bt, scale=w.scale, chunk=chunk, out=o, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    bits = torch.int32 if w.dtype == "f32" else torch.int16
+    assert torch.equal(outs[0][0].view(bits), outs[1][0].view(bits))
+    say("  fa_decode_splitkv (contiguous) %s chunk %d" % (w.name, chunk))
+    oc, lc = fa.decode_splitkv(qd, kc.cuda(), vc.cuda(), sl, scale=w.scale, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0].view(bits), oc.cpu().view(bits)), "paged differs from contiguous"
+    assert torch.equal(outs[0][1].view(torch.int32), lc.cpu().view(torch.int32))
+    o_ref, lse_ref = oracle.decode_paged(wl.to_f64(q), wl.to_f64(kp), wl.to_f64(vp), table, lens,
+                                         w.scale)
+    return assert_close(w.dtype, wl.to_f64(outs[0][0]), o_ref, outs[0][1].double().numpy(),
+                        lse_ref, "%s page %d chunk %d" % (w.name, page_size, chunk))
+
+
+PAGED = [
+    (wl.SMALL[5], 16, 256),
+    (dataclasses.replace(wl.SMALL[5], name="decode f16 D64 with empty caches", dtype="f16", D=64,
+                         seed=31, lens_fixed=[0, 1, 255, 256, 257, 2048]), 64, 64),
+    (dataclasses.replace(wl.SMALL[5], name="decode f32 D128", dtype="f32", seed=32, B=3), 32, 128),
+    (dataclasses.replace(wl.SMALL[5], name="decode bf16 D64", dtype="bf16", D=64, seed=33, B=3),
+     256, 512),
+    (dataclasses.replace(wl.SMALL[5], name="decode bf16 D128 one page", seed=34, B=2,
+                         lens_fixed=[1024, 700]), 1024, 256),
+]
+
+
+@pytest.mark.parametrize("w,page_size,chunk", PAGED,
+                         ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_decode_paged(w, page_size, chunk):
+    decode_paged_case(w, page_size, chunk)

@@ -350,6 +350,61 @@ def test_decode_is_one_noncausal_row():
     np.testing.assert_allclose(lse, lb[:, :, 0], atol=1e-13)
 
 
+def _scatter_pages(rng, kc, vc, lens, page_size, extra_pages=3):
+    """A page pool holding each entry's cache pages at shuffled positions,
+    NaN everywhere else, and the page table that finds them."""
+    B, nmax, H, D = kc.shape
+    per = -(-nmax // page_size)
+    n_pages = B * per + extra_pages
+    perm = rng.permutation(n_pages)
+    kp = np.full((n_pages, page_size, H, D), np.nan)
+    vp = np.full((n_pages, page_size, H, D), np.nan)
+    table = np.zeros((B, per), np.int32)
+    for b in range(B):
+        for i in range(per):
+            pg = int(perm[b * per + i])
+            table[b, i] = pg
+            rows = range(i * page_size, min((i + 1) * page_size, int(lens[b])))
+            for t in rows:
+                kp[pg, t - i * page_size] = kc[b, t]
+                vp[pg, t - i * page_size] = vc[b, t]
+    return kp, vp, table
+
+
+def test_decode_paged_is_decode_of_the_gathered_cache():
+    """Pages at shuffled pool positions, NaN in every unused page and row:
+    the paged decode equals the contiguous decode exactly."""
+    rng = np.random.default_rng(21)
+    B, H, D, nmax, ps = 4, 2, 4, 40, 16
+    q = rnd(rng, B, H, D)
+    kc, vc = rnd(rng, B, nmax, H, D), rnd(rng, B, nmax, H, D)
+    lens = np.array([40, 17, 1, 0])
+    kp, vp, table = _scatter_pages(rng, kc, vc, lens, ps)
+    o, lse = oracle.decode_paged(q, kp, vp, table, lens, 0.3)
+    oc, lc = oracle.decode(q, kc, vc, lens, 0.3)
+    assert np.array_equal(o, oc) and np.array_equal(lse, lc)
+    assert np.isfinite(o).all()
+    assert (o[3] == 0).all() and (lse[3] == -np.inf).all()  # an empty cache
+
+
+def test_decode_paged_brute_force():
+    """Pure-Python loop over keys reading rows through the table."""
+    rng = np.random.default_rng(22)
+    B, H, D, nmax, ps = 2, 2, 3, 37, 16
+    q = rnd(rng, B, H, D)
+    kc, vc = rnd(rng, B, nmax, H, D), rnd(rng, B, nmax, H, D)
+    lens = np.array([37, 20])
+    kp, vp, table = _scatter_pages(rng, kc, vc, lens, ps)
+    o, lse = oracle.decode_paged(q, kp, vp, table, lens, 0.7)
+    for b in range(B):
+        for h in range(H):
+            K = [list(map(float, kp[table[b][t // ps], t % ps, h])) for t in range(lens[b])]
+            V = [list(map(float, vp[table[b][t // ps], t % ps, h])) for t in range(lens[b])]
+            ob, lb = brute_row(list(map(float, q[b, h])), K, V, int(lens[b]), 0, 1, 0.7, False)
+            np.testing.assert_allclose(o[b, h], ob, atol=1e-13)
+            assert abs(lse[b, h] - lb) < 1e-13
+
+
 def test_golden_page_facts():
     """Numbers printed by the pages (see the fixture for citations)."""
     with open(os.path.join(GOLDEN, "page_facts.json")) as f:

@@ -61,6 +61,7 @@ class Workload:
     len_hi: int = 0
     value_scale: float = 1.0
     chunk: int = 256      # decode split size
+    page_size: int = 0    # paged decode: rows per cache page
     lens_fixed: Optional[Sequence[int]] = field(default=None, compare=False)
 
     def lengths(self) -> np.ndarray:
@@ -128,6 +129,11 @@ CFG = {
 }
 
 # Reduced shapes of the same kinds (several tiles plus ragged tails).
+# Beyond the table: the decode workload over a paged cache (16-row pages at
+# shuffled pool positions), the cache layout of serving runtimes.
+CFG[6] = replace(CFG[5], name="paged decode bf16 B64 H32 D128 Lk U[4096,32768] chunk 256 page 16",
+                 kind="paged", page_size=16)
+
 SMALL = {
     1: CFG[1],
     2: replace(CFG[2], name="bidirectional bf16 B2 H4 N700 D64", B=2, H=4, Nq=700, Nk=700),
@@ -205,7 +211,7 @@ def varlen_inputs(w: Workload):
 
 def decode_query(w: Workload):
     """q [B, H, D] (torch CPU, workload dtype)."""
-    assert w.kind == "decode"
+    assert w.kind in ("decode", "paged")
     return tensor(w, 0, (w.B, w.H, w.D))
 
 
@@ -230,6 +236,37 @@ def decode_inputs_cpu(w: Workload, pad_value: float = float("nan")):
         kc[b, :L] = decode_cache_rows(w, 1, b, L)
         vc[b, :L] = decode_cache_rows(w, 2, b, L)
     return q, kc, vc, lens.astype(np.int32)
+
+
+def page_layout(w: Workload, page_size: int, extra_pages: int = 5, seed: int = 0):
+    """A shuffled placement of each batch entry's cache pages in one pool.
+
+    Returns (block_table int32 [B, max_pages], num_pages): entry b's page i
+    is pool page block_table[b, i]; ``extra_pages`` pool pages belong to no
+    entry.  The permutation is ``default_rng(seed or w.seed).permutation``.
+    """
+    max_pages = -(-w.Nk // page_size)
+    num_pages = w.B * max_pages + extra_pages
+    perm = np.random.default_rng(seed or w.seed).permutation(num_pages)
+    table = perm[: w.B * max_pages].reshape(w.B, max_pages).astype(np.int32)
+    return table, num_pages
+
+
+def paged_from_cache(kc, vc, lens, table, num_pages, page_size, pad_value: float = float("nan")):
+    """Copy contiguous caches [B, Nk_max, H, D] into a page pool
+    [num_pages, page_size, H, D] laid out by ``table``; every pool row that
+    holds no real key is ``pad_value``."""
+    import torch
+    B, _, H, D = kc.shape
+    kp = torch.full((num_pages, page_size, H, D), pad_value, dtype=kc.dtype, device=kc.device)
+    vp = torch.full_like(kp, pad_value)
+    for b in range(B):
+        L = int(lens[b])
+        for i in range(-(-L // page_size)):
+            r0, r1 = i * page_size, min((i + 1) * page_size, L)
+            kp[int(table[b, i]), : r1 - r0] = kc[b, r0:r1]
+            vp[int(table[b, i]), : r1 - r0] = vc[b, r0:r1]
+    return kp, vp
 
 
 def to_f64(t) -> np.ndarray:
