@@ -14,6 +14,7 @@ attention, and works in float64 throughout.
 from .exact import (  # noqa: F401
     scores,
     visible,
+    alibi_bias,
     attention_rows,
     attention,
     attention_varlen,

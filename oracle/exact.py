@@ -62,22 +62,34 @@ def scores(q, k, scale):
     return float(scale) * (q @ k.T)
 
 
-def visible(q_pos, lq, lk, causal):
+def visible(q_pos, lq, lk, causal, prefix=0):
     """Boolean [n, lk]: may query row ``q_pos[r]`` (of ``lq`` rows) see key j?
 
     Keys j >= lk are padding and never visible (they are not even passed).
     With ``causal`` the mask is lower-triangular, bottom-right aligned:
     j <= i + lk - lq.  HF integration guide, 原因分析 item 1 and the
     parameter table's is_causal row; CANN explainer 代码讲解 causal branch.
+    The same item names the prefix mask: with ``prefix`` > 0 the first
+    ``prefix`` keys are seen by every query as well (bidirectional over the
+    prefix, causal after it).
     """
     q_pos = np.asarray(q_pos, dtype=np.int64).reshape(-1)
     j = np.arange(lk, dtype=np.int64)
     if not causal:
         return np.ones((q_pos.size, lk), dtype=bool)
-    return j[None, :] <= (q_pos[:, None] + (lk - lq))
+    return (j[None, :] <= (q_pos[:, None] + (lk - lq))) | (j[None, :] < prefix)
 
 
-def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal):
+def alibi_bias(q_pos, lq, lk, slope):
+    """Additive score bias [n, lk] of ALiBi, the other mask family that item
+    names: -slope * |j - p| with p = i + lk - lq the query's own key
+    position (for a causal row, slope * (j - p): linear in the distance)."""
+    q_pos = np.asarray(q_pos, dtype=np.int64).reshape(-1)
+    j = np.arange(lk, dtype=np.int64)
+    return -float(slope) * np.abs(j[None, :] - (q_pos[:, None] + (lk - lq))).astype(_F64)
+
+
+def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal, prefix=0, alibi_slope=None):
     """Output rows and log-sum-exp for a set of query rows of one (batch, head).
 
     q_rows: [n, D] query vectors; q_pos: [n] their row indices 0..lq-1;
@@ -86,7 +98,8 @@ def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal):
 
     Standard (materialised) attention for these rows: S, safe softmax P, O =
     P V.  Rows are independent, so computing a subset of rows gives exactly
-    the rows of the full result.
+    the rows of the full result.  ``prefix`` and ``alibi_slope`` select the
+    prefix mask and the ALiBi bias (see ``visible`` and ``alibi_bias``).
     """
     q_rows = np.asarray(q_rows, dtype=_F64)
     n, d = q_rows.shape
@@ -96,7 +109,10 @@ def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal):
     kk = np.asarray(k[:lk], dtype=_F64)
     vv = np.asarray(v[:lk], dtype=_F64)
     s = scores(q_rows, kk, scale)                       # [n, lk]
-    s = np.where(visible(q_pos, lq, lk, causal), s, -np.inf)
+    if alibi_slope is not None:
+        s = s + alibi_bias(q_pos, lq, lk, alibi_slope)
+    vis = visible(q_pos, lq, lk, causal, prefix) if prefix else visible(q_pos, lq, lk, causal)
+    s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)                                   # row maximum (safe softmax)
     empty = np.isneginf(m)                              # no visible key in the row
     m_shift = np.where(empty, 0.0, m)
@@ -110,11 +126,13 @@ def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal):
     return o, lse
 
 
-def attention(q, k, v, scale, causal, seqlens_k=None, row_chunk=1024):
+def attention(q, k, v, scale, causal, seqlens_k=None, row_chunk=1024, prefix=0,
+              alibi_slopes=None):
     """Batched attention in the library's BSHD layout.
 
     q: [B, Nq, H, D]; k, v: [B, Nk, H, D]; seqlens_k: optional [B] count of
     real keys per batch entry (the rest is padding); default Nk for all.
+    prefix: prefix-mask length (with causal); alibi_slopes: optional [H].
     Returns O [B, Nq, H, D] and lse [B, H, Nq] (float64).
     """
     q = np.asarray(q)
@@ -129,7 +147,8 @@ def attention(q, k, v, scale, causal, seqlens_k=None, row_chunk=1024):
             for r0 in range(0, nq, row_chunk):
                 r1 = min(nq, r0 + row_chunk)
                 ob, lb = attention_rows(q[b, r0:r1, h, :], np.arange(r0, r1), kb, vb,
-                                        nq, lk, scale, causal)
+                                        nq, lk, scale, causal, prefix,
+                                        None if alibi_slopes is None else alibi_slopes[h])
                 o[b, r0:r1, h, :] = ob
                 lse[b, h, r0:r1] = lb
     return o, lse

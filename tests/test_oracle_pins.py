@@ -428,6 +428,140 @@ def test_golden_page_facts():
 
 
 # ----------------------------------------------------------------------------
+# Prefix mask and ALiBi bias (the integration guide's other mask families)
+# ----------------------------------------------------------------------------
+
+def brute_masked_row(q, K, V, lk, i, lq, scale, causal, prefix, slope):
+    """Pure-Python row: visible keys under the causal + prefix mask, each
+    score plus -slope * |j - (i + lk - lq)|."""
+    pos = i + lk - lq
+    s = []
+    for j in range(lk):
+        if causal and j > pos and j >= prefix:
+            continue
+        s.append((math.fsum(q[d] * K[j][d] for d in range(len(q))) * scale - slope * abs(j - pos), j))
+    if not s:
+        return [0.0] * len(V[0]), -math.inf
+    mx = max(x for x, _ in s)
+    w = [(math.exp(x - mx), j) for x, j in s]
+    den = math.fsum(e for e, _ in w)
+    return [math.fsum(e * V[j][d] for e, j in w) / den for d in range(len(V[0]))], mx + math.log(den)
+
+
+@pytest.mark.parametrize("nq,nk,prefix,slopes,causal", [
+    (5, 5, 2, None, True), (4, 7, 3, None, True), (6, 4, 1, None, True), (5, 5, 9, None, True),
+    (5, 5, 0, [0.3, 1.1], True), (4, 6, 2, [0.5, 0.0], True), (5, 5, 0, [0.25, 2.0], False),
+    (3, 7, 0, [0.7, 0.1], False),
+])
+def test_prefix_and_alibi_brute_force(nq, nk, prefix, slopes, causal):
+    rng = np.random.default_rng(31 + nq * 7 + nk + prefix)
+    B, H, D = 2, 2, 3
+    q, k, v = rnd(rng, B, nq, H, D), rnd(rng, B, nk, H, D), rnd(rng, B, nk, H, D)
+    sl = None if slopes is None else np.array(slopes)
+    o, lse = oracle.attention(q, k, v, 0.6, causal, prefix=prefix, alibi_slopes=sl)
+    for b in range(B):
+        for h in range(H):
+            K = [list(map(float, k[b, j, h])) for j in range(nk)]
+            V = [list(map(float, v[b, j, h])) for j in range(nk)]
+            for i in range(nq):
+                ob, lb = brute_masked_row(list(map(float, q[b, i, h])), K, V, nk, i, nq, 0.6,
+                                          causal, prefix, 0.0 if sl is None else sl[h])
+                np.testing.assert_allclose(o[b, i, h], ob, atol=1e-13)
+                assert lse[b, h, i] == lb or abs(lse[b, h, i] - lb) < 1e-13
+
+
+def test_prefix_mask_special_cases():
+    """prefix 0 is the causal mask; a prefix covering every key is no mask."""
+    rng = np.random.default_rng(41)
+    q, k, v = rnd(rng, 2, 6, 2, 4), rnd(rng, 2, 6, 2, 4), rnd(rng, 2, 6, 2, 4)
+    a = oracle.attention(q, k, v, 0.5, True, prefix=0)
+    b = oracle.attention(q, k, v, 0.5, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = oracle.attention(q, k, v, 0.5, True, prefix=6)
+    d = oracle.attention(q, k, v, 0.5, False)
+    np.testing.assert_allclose(c[0], d[0], atol=1e-14)
+    np.testing.assert_allclose(c[1], d[1], atol=1e-14)
+
+
+def test_alibi_special_cases():
+    """Slope 0 is no bias; a huge slope leaves only the key at the query's own
+    position, so the row is that key's value and the log-sum-exp its score."""
+    rng = np.random.default_rng(42)
+    nq, nk = 4, 6
+    q, k, v = rnd(rng, 1, nq, 2, 4), rnd(rng, 1, nk, 2, 4), rnd(rng, 1, nk, 2, 4)
+    a = oracle.attention(q, k, v, 0.5, True, alibi_slopes=np.zeros(2))
+    b = oracle.attention(q, k, v, 0.5, True)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-15)
+    for causal in (True, False):
+        o, lse = oracle.attention(q, k, v, 0.5, causal, alibi_slopes=np.array([1e4, 1e4]))
+        for i in range(nq):
+            p = i + nk - nq
+            np.testing.assert_allclose(o[0, i], v[0, p], atol=1e-12)
+            for h in range(2):
+                assert abs(lse[0, h, i] - 0.5 * float(q[0, i, h] @ k[0, p, h])) < 1e-9
+
+
+def test_causal_alibi_is_attention_on_augmented_vectors():
+    """For causal rows the bias slope*(j - p) is slope*j plus a per-row
+    constant, which softmax ignores: it equals plain attention after appending
+    1 to every query and slope*j/scale to key j (lse shifted by slope*p)."""
+    rng = np.random.default_rng(43)
+    nq, nk, D, scale, slope = 5, 8, 3, 0.4, 0.35
+    q, k, v = rnd(rng, 1, nq, 1, D), rnd(rng, 1, nk, 1, D), rnd(rng, 1, nk, 1, D)
+    o, lse = oracle.attention(q, k, v, scale, True, alibi_slopes=np.array([slope]))
+    qa = np.concatenate([q, np.ones((1, nq, 1, 1))], axis=-1)
+    ka = np.concatenate([k, (slope * np.arange(nk) / scale).reshape(1, nk, 1, 1)], axis=-1)
+    o2, lse2 = oracle.attention(qa, ka, v, scale, True)
+    np.testing.assert_allclose(o, o2, atol=1e-13)
+    p = np.arange(nq) + nk - nq
+    np.testing.assert_allclose(lse[0, 0], lse2[0, 0] - slope * p, atol=1e-13)
+
+
+def _alibi_sign_flip(q_pos, lq, lk, slope):
+    q_pos = np.asarray(q_pos).reshape(-1)
+    return float(slope) * np.abs(np.arange(lk)[None, :] - (q_pos[:, None] + lk - lq)).astype(float)
+
+
+def _alibi_top_left(q_pos, lq, lk, slope):
+    q_pos = np.asarray(q_pos).reshape(-1)
+    return -float(slope) * np.abs(np.arange(lk)[None, :] - q_pos[:, None]).astype(float)
+
+
+def _vis_prefix_inclusive(q_pos, lq, lk, causal, prefix=0):
+    q_pos = np.asarray(q_pos).reshape(-1)
+    j = np.arange(lk)
+    if not causal:
+        return np.ones((q_pos.size, lk), bool)
+    return (j[None, :] <= q_pos[:, None] + lk - lq) | (j[None, :] <= prefix)
+
+
+_MASK_PINS = [
+    lambda: test_prefix_and_alibi_brute_force(5, 5, 2, None, True),
+    lambda: test_prefix_and_alibi_brute_force(6, 4, 1, None, True),
+    lambda: test_prefix_and_alibi_brute_force(4, 6, 2, [0.5, 0.0], True),
+    lambda: test_prefix_and_alibi_brute_force(3, 7, 0, [0.7, 0.1], False),
+    test_alibi_special_cases,
+    test_causal_alibi_is_attention_on_augmented_vectors,
+]
+
+
+@pytest.mark.parametrize("name,attr,bad", [
+    ("alibi sign flipped", "alibi_bias", _alibi_sign_flip),
+    ("alibi position top-left", "alibi_bias", _alibi_top_left),
+    ("prefix bound inclusive", "visible", _vis_prefix_inclusive),
+])
+def test_planted_mask_mistakes_are_caught(monkeypatch, name, attr, bad):
+    monkeypatch.setattr(oa, attr, bad)
+    caught = 0
+    for pin in _MASK_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake: {name}"
+
+
+# ----------------------------------------------------------------------------
 # Planted mistakes: each must be caught by at least one pin above
 # ----------------------------------------------------------------------------
 
@@ -439,7 +573,7 @@ def _sign_flip(q, k, scale):
     return -float(scale) * (np.asarray(q, float) @ np.asarray(k, float).T)
 
 
-def _vis_strict(q_pos, lq, lk, causal):
+def _vis_strict(q_pos, lq, lk, causal, prefix=0):
     q_pos = np.asarray(q_pos).reshape(-1)
     j = np.arange(lk)
     if not causal:
@@ -447,7 +581,7 @@ def _vis_strict(q_pos, lq, lk, causal):
     return j[None, :] < (q_pos[:, None] + lk - lq)
 
 
-def _vis_top_left(q_pos, lq, lk, causal):
+def _vis_top_left(q_pos, lq, lk, causal, prefix=0):
     q_pos = np.asarray(q_pos).reshape(-1)
     j = np.arange(lk)
     if not causal:
