@@ -136,7 +136,12 @@ def run_config(n, args, dev):
         q, k, v = make_prefill(w, dev)
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-        call = lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if w.prefix or w.alibi:
+            sd = torch.from_numpy(wl.alibi_slopes(w.H)).to(dev) if w.alibi else None
+            call = lambda: fa.fwd_masked(q, k, v, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                                         alibi_slopes=sd, out=o, lse=lse)
+        else:
+            call = lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
     elif w.kind == "varlen":
         q, k, v, cu = wl.varlen_inputs(w)
         q, k, v = q.to(dev), k.to(dev), v.to(dev)
@@ -206,10 +211,11 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
-    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5, 6], default=None,
+    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5, 6, 7, 8], default=None,
                     help="time one workload alone (its library call only) and print a JSON "
                          "line for it instead of the bench line: 1-5 the benchmark table, "
-                         "6 its decode over a paged cache")
+                         "6 its decode over a paged cache, 7 / 8 its N8192 causal prefill "
+                         "with a 2048-key prefix mask / with ALiBi")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "

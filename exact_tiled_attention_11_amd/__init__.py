@@ -26,9 +26,9 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
-    "fa_fwd", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
+    "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
-    "fwd", "fwd_varlen", "decode_splitkv", "decode_splitkv_paged",
+    "fwd", "fwd_masked", "fwd_varlen", "decode_splitkv", "decode_splitkv_paged",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -40,6 +40,8 @@ _LIB: Optional[ctypes.CDLL] = None
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp]),
+    "fa_fwd_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _i,
+                           _vp]),
     "fa_fwd_varlen_workspace_bytes": (_sz, [_i, _i]),
     "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                            _sz, _i, _vp]),
@@ -88,6 +90,12 @@ def load() -> ctypes.CDLL:
 
 def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, dtype, stream) -> int:
     return load().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, dtype, stream)
+
+
+def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix, alibi_slopes,
+                  dtype, stream) -> int:
+    return load().fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
+                                alibi_slopes, dtype, stream)
 
 
 def fa_fwd_varlen_workspace_bytes(nseq, total_q) -> int:
@@ -180,6 +188,32 @@ def fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens
     st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D, float(scale),
                 int(bool(causal)), _ptr(seqlens_k), _dtype_code(q), _stream(stream))
     _check("fa_fwd", st)
+    return out, lse
+
+
+def fwd_masked(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
+               prefix: int = 0, alibi_slopes=None, out=None, lse=None, return_lse: bool = True,
+               stream=None) -> Tuple:
+    """fwd with the prefix mask (causal only) and/or ALiBi slopes (float32 [H] on the device)."""
+    import torch
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H):
+        raise ValueError("alibi_slopes must be float32[H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
+        raise ValueError("seqlens_k must be int32[B]")
+    st = fa_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D,
+                       float(scale), int(bool(causal)), _ptr(seqlens_k), int(prefix),
+                       _ptr(alibi_slopes), _dtype_code(q), _stream(stream))
+    _check("fa_fwd_masked", st)
     return out, lse
 
 

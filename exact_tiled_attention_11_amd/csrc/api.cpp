@@ -65,17 +65,21 @@ const char* fa_status_string(fa_status_t s) {
 
 const char* fa_version(void) { return "libfa355 0.1.0 (gfx950)"; }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                   int H, int Nq, int Nk, int D, float scale, int causal,
-                   const int32_t* seqlens_k, fa_dtype_t dtype, void* stream) {
+fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                          const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
+                          fa_dtype_t dtype, void* stream) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  // the mask families are implemented by the 16-bit kernel only
+  if (dtype == FA_F32 && (prefix != 0 || alibi_slopes)) return FA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if ((causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  if (prefix < 0 || (prefix > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (Nq == 0) return FA_OK;
   if (!q || !o || ((!k || !v) && Nk > 0)) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(seqlens_k))
+      !aligned16(seqlens_k) || ((uintptr_t)alibi_slopes & 3u) != 0)
     return FA_ERR_INVALID_ARG;
   // element offsets must fit the kernels' 64-bit address math and grid limits
   const int rows = fa::fwd_block_rows(dtype, D);
@@ -101,8 +105,17 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   a.Nk = Nk;
   a.nqb = (int)nqb;
   a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
+  a.prefix = prefix;
+  a.alibi = alibi_slopes;
   return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, false, (unsigned)grid,
                                  (hipStream_t)stream));
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Nq, int Nk, int D, float scale, int causal,
+                   const int32_t* seqlens_k, fa_dtype_t dtype, void* stream) {
+  return fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, 0, nullptr,
+                       dtype, stream);
 }
 
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {

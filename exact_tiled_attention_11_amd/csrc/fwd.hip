@@ -550,7 +550,7 @@ struct PipeCfg {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdArgs a) {
   using C = PipeCfg<T, D, NW, PK>;
   using E = Elem<T>;
@@ -579,12 +579,17 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   WorkItem wi;
   if (!work_item<CAUSAL, VARLEN>(a, wi)) return;  // whole workgroup leaves together
   const int lq = wi.lq, lk = wi.lk;
+  float slope2 = 0.f;  // ALiBi slope of this head, in exp2 units
+  if constexpr (ALIBI) slope2 = a.alibi[wi.h] * kLog2e;
 
   const int q0 = wi.qblk * C::kBR;
   const int off = lk - lq;  // bottom-right causal alignment
+  // Under the causal mask row i sees keys 0 .. max(i + off, prefix - 1): the
+  // prefix keys are seen by every row, so the visible keys stay a prefix.
+  const int pre = a.prefix - 1;
   int nst = (lk + C::kBC - 1) / C::kBC;  // key blocks of the workgroup
   if (CAUSAL) {
-    const int kmax = min(q0 + C::kBR, lq) - 1 + off;
+    const int kmax = max(min(q0 + C::kBR, lq) - 1 + off, pre);
     nst = kmax < 0 ? 0 : min(nst, kmax / C::kBC + 1);
   }
   const int wq0 = q0 + wave * 32;
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   if (wq_last >= wq0) {
     nw = nst;
     if (CAUSAL) {
-      const int t = wq_last + off;
+      const int t = max(wq_last + off, pre);
       nw = t < 0 ? 0 : min(nst, t / C::kBC + 1);
     }
   }
@@ -673,7 +678,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   asm volatile("" : "+s"(nwp));
   auto need_mask = [&](int u) __attribute__((always_inline)) {
     const int k0 = u * C::kBC;
-    return (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > wq0 + off);
+    return (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > max(wq0 + off, pre));
   };
 
   // Register roles (fixed, so nothing is copied between blocks):
@@ -766,11 +771,38 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
     const float ms = mrow == -INFINITY ? 0.f : mrow;
+    // ALiBi: -slope * |key - position| in exp2 units, key 8*(r>>2) + 4*hh +
+    // (r&3) of the block, position qi + off.  In a causal block left of the
+    // wave's first row every key is at or before the position, so the bias is
+    // slope * (key - position): a per-lane part joins the exponent's addend
+    // and the per-element part slope * (8*(r>>2) + (r&3)) is one FMA with a
+    // literal.  Other blocks take the absolute value (two operations).
+    float addend = -ms;
+    bool lin = false;
+    float dbase = 0.f;
+    if constexpr (ALIBI) {
+      dbase = (float)(u * C::kBC + 4 * hh - (wq0 + col + off));
+      lin = CAUSAL && (u * C::kBC + C::kBC - 1 <= wq0 + off);
+      if (lin) addend = __builtin_fmaf(slope2, dbase, addend);
+    }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sX[r] = __builtin_fmaf(sS[r], a.c, -ms);
+    for (int r = 0; r < 16; ++r) sX[r] = __builtin_fmaf(sS[r], a.c, addend);
+    if constexpr (ALIBI) {
+      if (lin) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sX[r] = __builtin_fmaf(slope2, (float)(8 * (r >> 2) + (r & 3)), sX[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float d = dbase + (float)(8 * (r >> 2) + (r & 3));
+          sX[r] = __builtin_fmaf(-slope2, fabsf(d), sX[r]);
+        }
+      }
+    }
     if (masked) {
       const int qi = wq0 + col;
-      const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;
+      const int last = CAUSAL ? min(max(qi + off, pre), lk - 1) : lk - 1;
       const float base = (float)(last - u * C::kBC - 4 * hh) * 0x1p110f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -1008,12 +1040,16 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
   if constexpr (UsePipe<T, D>::value) {
     constexpr int NW = 4, PK = FA_PIPE_PK;
     constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
-    if (causal) {
-      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true>, grid, NW * 64, lds, stream, a);
-      return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false>, grid, NW * 64, lds, stream, a);
+    if (a.alibi) {  // fixed-length only (the entry point checks)
+      if (causal) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, true>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, true>, grid, NW * 64, lds, stream, a);
     }
-    if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true>, grid, NW * 64, lds, stream, a);
-    return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false>, grid, NW * 64, lds, stream, a);
+    if (causal) {
+      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, false>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, false>, grid, NW * 64, lds, stream, a);
+    }
+    if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, false>, grid, NW * 64, lds, stream, a);
+    return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, false>, grid, NW * 64, lds, stream, a);
   }
   using Tl = Tile<T, D>;
   constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;

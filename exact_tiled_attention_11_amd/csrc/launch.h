@@ -24,6 +24,9 @@ struct FwdArgs {
   int nqb;                 // fixed-length: query blocks per (batch, head)
   int total_q;             // varlen: lse row stride
   float c;                 // scale * log2(e)
+  // mask families (16-bit fixed-length prefill only; zero / null otherwise)
+  int prefix;              // with causal: keys [0, prefix) are seen by every query
+  const float* alibi;      // [H] slopes: score += -slope_h * |j - (i + Lk - Lq)|
 };
 
 // Query rows per workgroup and keys per tile of the prefill kernel instance

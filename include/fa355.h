@@ -83,6 +83,27 @@ FA355_API fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* 
                    const int32_t* seqlens_k, fa_dtype_t dtype, void* stream);
 
 /*
+ * Fixed-length attention with the other mask families the Hugging Face
+ * Flash-Attention-2 integration guide names (原因分析, item 1: prefix mask,
+ * ALiBi).  Arguments as fa_fwd, plus:
+ *   prefix: >= 0; only with causal = 1 (else FA_ERR_INVALID_ARG).  Keys
+ *       0 .. prefix-1 are seen by every query as well (bidirectional over the
+ *       prefix, causal after it): query i sees key j iff
+ *       j <= i + Lk - Lq or j < prefix.  0 = plain causal.
+ *   alibi_slopes: device float[H] or NULL (4-byte aligned).  If given, the
+ *       score of query i and key j is scale * q.k - slope_h * |j - (i + Lk - Lq)|
+ *       (for causal rows the usual slope_h * (j - i) form, up to a per-row
+ *       constant that softmax ignores); lse includes the bias.
+ * fp16 and bf16 only: fp32 with a prefix or slopes is FA_ERR_UNSUPPORTED.
+ * fa_fwd(...) is fa_fwd_masked(..., 0, NULL, ...).
+ */
+FA355_API fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int H, int Nq, int Nk, int D,
+                                    float scale, int causal, const int32_t* seqlens_k,
+                                    int prefix, const float* alibi_slopes,
+                                    fa_dtype_t dtype, void* stream);
+
+/*
  * Packed variable-length attention (the guide's flash_attn_varlen, FAQ 4).
  *   q   : [total_q, H, D];  k, v: [total_k, H, D];  o: like q
  *   lse : [H, total_q] float32 or NULL

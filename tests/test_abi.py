@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
-        "fa_fwd", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
+        "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes",
+        "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
         "fa_version"])
 
@@ -122,6 +123,25 @@ def test_decode_validation():
     assert call(wsb=100) == fa.FA_ERR_WORKSPACE
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(o=MIS) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fwd_masked_validation():
+    base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=64, Nk=64, D=64, scale=0.1, causal=1,
+                sl=None, prefix=8, alibi=P, dtype=fa.FA_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                a["Nk"], a["D"], a["scale"], a["causal"], a["sl"], a["prefix"],
+                                a["alibi"], a["dtype"], a["stream"])
+    assert call(prefix=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(causal=0) == fa.FA_ERR_INVALID_ARG              # a prefix needs the causal mask
+    assert call(alibi=P + 2) == fa.FA_ERR_INVALID_ARG           # float slopes not 4-byte aligned
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED       # mask families are 16-bit only
+    assert call(dtype=fa.FA_F32, prefix=0) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(Nq=0) == fa.FA_OK                               # nothing to do, no device needed
 
 
 def test_decode_paged_validation():

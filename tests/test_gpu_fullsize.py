@@ -40,16 +40,24 @@ def _sample_rows(rng, n, extra=()):
     return sorted(base)
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 7, 8])
 def test_prefill_full_size_sampled(cfg):
     fa = _fa()
     w = wl.CFG[cfg]
     say("generate %s" % w.name)
     q, k, v = wl.prefill_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    slopes = wl.alibi_slopes(w.H) if w.alibi else None
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+
+    def call():
+        if w.prefix or w.alibi:
+            return fa.fwd_masked(qd, kd, vd, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                                 alibi_slopes=sd)
+        return fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
     say("fa_fwd %s" % w.name)
-    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
-    o2, lse2 = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    o, lse = call()
+    o2, lse2 = call()
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
@@ -61,7 +69,8 @@ def test_prefill_full_size_sampled(cfg):
         rows = _sample_rows(rng, w.Nq)
         kb, vb = wl.to_f64(k[b, :, h]), wl.to_f64(v[b, :, h])
         qr = wl.to_f64(q[b, rows, h])
-        o_ref, lse_ref = oracle.attention_rows(qr, rows, kb, vb, w.Nq, w.Nk, w.scale, w.causal)
+        o_ref, lse_ref = oracle.attention_rows(qr, rows, kb, vb, w.Nq, w.Nk, w.scale, w.causal,
+                                               w.prefix, None if slopes is None else float(slopes[h]))
         assert_close(w.dtype, wl.to_f64(o_c[b, rows, h]), o_ref, lse_c[b, h, rows].double().numpy(),
                      lse_ref, "%s b%d h%d" % (w.name, b, h))
 

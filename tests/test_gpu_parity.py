@@ -232,3 +232,56 @@ PAGED = [
                          ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_decode_paged(w, page_size, chunk):
     decode_paged_case(w, page_size, chunk)
+
+
+def masked_case(w, seqlens=None, slope_mul=1.0):
+    """fa_fwd_masked (prefix mask and/or ALiBi) against the oracle."""
+    fa = _fa()
+    q, k, v = wl.prefill_inputs(w)
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            k[b, L:] = float("nan")
+            v[b, L:] = float("nan")
+    slopes = wl.alibi_slopes(w.H) * slope_mul if w.alibi else None
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    outs = []
+    for rep in range(2):
+        o = torch.full_like(qd, float("nan"))
+        lse = torch.full((w.B, w.H, w.Nq), float("nan"), dtype=torch.float32, device="cuda")
+        say("  fa_fwd_masked %s prefix %d alibi %s rep %d" % (w.name, w.prefix, w.alibi, rep))
+        fa.fwd_masked(qd, kd, vd, causal=w.causal, scale=w.scale, seqlens_k=sl, prefix=w.prefix,
+                      alibi_slopes=sd, out=o, lse=lse)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    (o1, l1), (o2, l2) = outs
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    o_ref, lse_ref = oracle.attention(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), w.scale, w.causal,
+                                      seqlens_k=seqlens, prefix=w.prefix,
+                                      alibi_slopes=None if slopes is None else slopes.astype(np.float64))
+    return assert_close(w.dtype, wl.to_f64(o1), o_ref, l1.double().numpy(), lse_ref, w.name)
+
+
+MASKED = [
+    (dataclasses.replace(wl.SMALL[3], name="bf16 D64 causal N1000 prefix 300", prefix=300), None, 1.0),
+    (dataclasses.replace(P("f16 D128 causal Nq500 Nk700 prefix 260", "f16", 128, True, 2, 2, 500, 700,
+                           seed=41), prefix=260), None, 1.0),
+    (dataclasses.replace(P("bf16 D64 causal N300 prefix past every key", "bf16", 64, True, 1, 2, 300,
+                           300, seed=42), prefix=400), None, 1.0),
+    (dataclasses.replace(P("bf16 D64 causal Nq300 Nk100 prefix 50 (rows see only the prefix)",
+                           "bf16", 64, True, 1, 2, 300, 100, seed=43), prefix=50), None, 1.0),
+    (dataclasses.replace(wl.SMALL[3], name="bf16 D64 causal N1000 ALiBi", alibi=True), None, 1.0),
+    (dataclasses.replace(P("bf16 D128 noncausal N333 ALiBi", "bf16", 128, False, 2, 4, 333, 333,
+                           seed=44), alibi=True), None, 1.0),
+    (dataclasses.replace(P("f16 D64 causal N700 prefix 128 + ALiBi, padded keys", "f16", 64, True, 2,
+                           4, 700, 700, seed=45), prefix=128, alibi=True), [700, 523], 1.0),
+    (dataclasses.replace(P("bf16 D64 causal N400 ALiBi steep slopes", "bf16", 64, True, 1, 4, 400,
+                           400, seed=46), alibi=True), None, 40.0),
+]
+
+
+@pytest.mark.parametrize("w,seqlens,slope_mul", MASKED, ids=lambda x: getattr(x, "name", str(x)))
+def test_masked(w, seqlens, slope_mul):
+    masked_case(w, seqlens, slope_mul)

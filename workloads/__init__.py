@@ -62,6 +62,8 @@ class Workload:
     value_scale: float = 1.0
     chunk: int = 256      # decode split size
     page_size: int = 0    # paged decode: rows per cache page
+    prefix: int = 0       # prefill with the prefix mask: keys every query sees
+    alibi: bool = False   # prefill with ALiBi: slopes of alibi_slopes(H)
     lens_fixed: Optional[Sequence[int]] = field(default=None, compare=False)
 
     def lengths(self) -> np.ndarray:
@@ -82,7 +84,7 @@ class Workload:
 
     def visible_pairs_per_head(self) -> int:
         if self.kind == "prefill":
-            return self.B * _pairs(self.Nq, self.Nk, self.causal)
+            return self.B * _pairs(self.Nq, self.Nk, self.causal, self.prefix)
         if self.kind == "varlen":
             return int(sum(_pairs(int(L), int(L), self.causal) for L in self.lengths()))
         return int(self.lengths().sum())
@@ -101,14 +103,14 @@ class Workload:
         return 2 * tot_k * row + 2 * self.B * row + self.B * self.H * 4
 
 
-def _pairs(nq: int, nk: int, causal: bool) -> int:
+def _pairs(nq: int, nk: int, causal: bool, prefix: int = 0) -> int:
     if not causal:
         return nq * nk
     off = nk - nq
     total = 0
-    # rows i with i + off >= 0 see min(nk, i + off + 1) keys
+    # row i sees keys 0 .. max(i + off, prefix - 1), at most nk of them
     for i in range(nq):
-        total += max(0, min(nk, i + off + 1))
+        total += max(0, min(nk, max(i + off, prefix - 1) + 1))
     return total
 
 
@@ -129,6 +131,11 @@ CFG = {
 }
 
 # Reduced shapes of the same kinds (several tiles plus ragged tails).
+# Beyond the table: the N8192 causal prefill with the prefix mask (the first
+# 2048 keys bidirectional) and with ALiBi slopes.
+CFG[7] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 prefix 2048", prefix=2048)
+CFG[8] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 ALiBi", alibi=True)
+
 # Beyond the table: the decode workload over a paged cache (16-row pages at
 # shuffled pool positions), the cache layout of serving runtimes.
 CFG[6] = replace(CFG[5], name="paged decode bf16 B64 H32 D128 Lk U[4096,32768] chunk 256 page 16",
@@ -236,6 +243,12 @@ def decode_inputs_cpu(w: Workload, pad_value: float = float("nan")):
         kc[b, :L] = decode_cache_rows(w, 1, b, L)
         vc[b, :L] = decode_cache_rows(w, 2, b, L)
     return q, kc, vc, lens.astype(np.int32)
+
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """The ALiBi paper's head slopes: the geometric sequence 2^(-8 (h+1) / H),
+    float32 [H] (for a power-of-two head count)."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
 
 
 def page_layout(w: Workload, page_size: int, extra_pages: int = 5, seed: int = 0):
