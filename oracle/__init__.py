@@ -17,6 +17,7 @@ from .exact import (  # noqa: F401
     alibi_bias,
     attention_rows,
     attention,
+    attention_bwd,
     attention_varlen,
     decode,
     decode_paged,

@@ -154,6 +154,53 @@ def attention(q, k, v, scale, causal, seqlens_k=None, row_chunk=1024, prefix=0,
     return o, lse
 
 
+def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None):
+    """Gradients of the forward definition: given dO = dL/dO, returns
+    (dQ, dK, dV) in the BSHD layout, float64.
+
+    The CSDN primer 轻松读懂FlashAttention 上, section Softmax求解重构: with
+    tiling and recompute, storing O and the row statistics is enough for the
+    backward pass, which recomputes P instead of storing it.  What it
+    computes is the chain rule through S = scale Q Kᵀ (masked), P = softmax
+    rows of S, O = P V, written out here with S and P materialised:
+      dV = Pᵀ dO;  dP = dO Vᵀ;  dS = P ∘ (dP - rowsum(dO ∘ O));
+      dQ = scale dS K;  dK = scale dSᵀ Q.
+    Masked pairs have P = 0 and so no gradient; keys >= Lk (padding) get
+    dK = dV = 0; a row with no visible key contributes nothing.
+    """
+    q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
+    B, nq, H, D = q.shape
+    nk = k.shape[1]
+    dq = np.zeros(q.shape, _F64)
+    dk = np.zeros(k.shape, _F64)
+    dv = np.zeros(v.shape, _F64)
+    for b in range(B):
+        lk = nk if seqlens_k is None else int(seqlens_k[b])
+        if lk == 0:
+            continue
+        for h in range(H):
+            qq = np.asarray(q[b, :, h], _F64)
+            kk = np.asarray(k[b, :lk, h], _F64)
+            vv = np.asarray(v[b, :lk, h], _F64)
+            g = np.asarray(do[b, :, h], _F64)
+            s = scores(qq, kk, scale)
+            vis = visible(np.arange(nq), nq, lk, causal)
+            s = np.where(vis, s, -np.inf)
+            m = s.max(axis=1)
+            m_shift = np.where(np.isneginf(m), 0.0, m)
+            e = np.exp(s - m_shift[:, None])
+            ell = e.sum(axis=1)
+            p = np.where(ell[:, None] > 0, e / np.where(ell > 0, ell, 1.0)[:, None], 0.0)
+            o = p @ vv
+            dv[b, :lk, h] = p.T @ g
+            dp = g @ vv.T
+            delta = (g * o).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dq[b, :, h] = float(scale) * (ds @ kk)
+            dk[b, :lk, h] = float(scale) * (ds.T @ qq)
+    return dq, dk, dv
+
+
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, row_chunk=1024):
     """Packed variable-length attention (the guide's flash_attn_varlen, FAQ 4).
 
