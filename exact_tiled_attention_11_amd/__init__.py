@@ -26,9 +26,9 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
-    "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
+    "fa_fwd", "fa_fwd_masked", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
-    "fwd", "fwd_masked", "fwd_varlen", "decode_splitkv", "decode_splitkv_paged",
+    "fwd", "fwd_masked", "bwd", "fwd_varlen", "decode_splitkv", "decode_splitkv_paged",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -42,6 +42,9 @@ _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp]),
     "fa_fwd_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _i,
                            _vp]),
+    "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
+                    _vp, _sz, _i, _vp]),
     "fa_fwd_varlen_workspace_bytes": (_sz, [_i, _i]),
     "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                            _sz, _i, _vp]),
@@ -96,6 +99,16 @@ def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, pr
                   dtype, stream) -> int:
     return load().fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
                                 alibi_slopes, dtype, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, Nq) -> int:
+    return load().fa_bwd_workspace_bytes(B, H, Nq)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, workspace,
+           workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal,
+                         seqlens_k, workspace, workspace_bytes, dtype, stream)
 
 
 def fa_fwd_varlen_workspace_bytes(nseq, total_q) -> int:
@@ -215,6 +228,27 @@ def fwd_masked(q, k, v, *, causal: bool = False, scale: Optional[float] = None, 
                        _ptr(alibi_slopes), _dtype_code(q), _stream(stream))
     _check("fa_fwd_masked", st)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
+        seqlens_k=None, dq=None, dk=None, dv=None, workspace=None, stream=None) -> Tuple:
+    """Gradients (dq, dk, dv) for the forward fwd(q, k, v) that produced o and lse, given dout."""
+    import torch
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
+                                device=q.device)
+    st = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)), _ptr(seqlens_k),
+                _ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
+    _check("fa_bwd", st)
+    return dq, dk, dv
 
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,

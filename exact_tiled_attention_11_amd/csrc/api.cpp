@@ -118,6 +118,62 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                        dtype, stream);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
+  if (B < 1 || H < 1 || Nq < 0) return 0;
+  const size_t n = (size_t)B * H * (Nq > 0 ? Nq : 1);
+  return (n * 4 + 255) / 256 * 256;
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                   int D, float scale, int causal, const int32_t* seqlens_k, void* workspace,
+                   size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit only
+  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (Nq == 0 && Nk == 0) return FA_OK;
+  if ((Nq > 0 && (!q || !o || !lse || !dout || !dq)) || (Nk > 0 && (!k || !v || !dk || !dv)))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse) ||
+      !aligned16(seqlens_k) || !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  const long long rows = fa::bwd_block_rows();
+  const long long nbh = (long long)B * H;
+  if (((long long)Nq + rows - 1) / rows * nbh > 0x7fffffffLL ||
+      ((long long)Nk + rows - 1) / rows * nbh > 0x7fffffffLL)
+    return FA_ERR_INVALID_ARG;
+  if ((long long)B * Nq * H > 0x7fffffffLL * 256LL) return FA_ERR_INVALID_ARG;
+  if ((long long)B * Nq > 0x7fffffffLL || (long long)B * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq)) return FA_ERR_WORKSPACE;
+
+  fa_status_t st = device_ok();
+  if (st != FA_OK) return st;
+
+  fa::BwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = (float*)workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.seqlens_k = seqlens_k;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.nqb = (int)((Nq + rows - 1) / rows);
+  a.c = fmaxf(scale * kLog2eF, 1e-30f);  // the forward's exponent scale
+  a.scale = scale;
+  return from_hip(fa::launch_bwd(a, dtype, D, causal != 0, (hipStream_t)stream));
+}
+
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
   if (nseq < 1 || total_q < 0) return 0;
   // the smallest query block of any instance bounds the tile count from above

@@ -1,0 +1,522 @@
+// Backward pass of libfa355: dQ, dK, dV from Q, K, V, O, lse and dO.
+//
+// The CSDN primer 轻松读懂FlashAttention 上, section Softmax求解重构, names the
+// two techniques of the method, tiling and recompute: because O and the row
+// statistics are stored, the backward pass recomputes the probabilities
+// block by block instead of keeping the N x N matrix P.  With lse = m + ln l
+// a probability is exp(s - lse) directly.  The gradients are the chain rule
+// through S = scale Q K^T (masked), P = row softmax of S, O = P V:
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - delta),  delta = rowsum(dO o O),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// gfx950 mapping (ours):
+//  * delta: one thread per (batch, query, head) row.
+//  * dK/dV: one workgroup per 128 keys of one (batch, head), a wave per 32
+//    keys holding its K and V rows in VGPRs as MFMA B operands; 32-row chunks
+//    of Q and dO (with lse and delta) stream through LDS, double buffered.
+//    Lanes own key columns: S = Q K^T and dP = dO V^T come out of the MFMA
+//    with the chunk's queries along the registers, so P and dS are packed in
+//    place as the B operand of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//    operands are transposing reads (ds_read_b64_tr_b16) of the same LDS tiles.
+//  * dQ: one workgroup per 128 query rows (a wave per 32), Q and dO in
+//    VGPRs, 32-key blocks of K and V streaming through LDS; lanes own query
+//    columns, as in the forward kernel, and dQ^T += K^T dS^T.
+//  * Rows past the end, rows with no visible key (lse = -inf) and padding
+//    keys get a probability of exactly 0; padding keys get dK = dV = 0.
+//  * Tiles are staged through VGPRs with ordinary loads (the compiler counts
+//    the waits); every result is written once, with no atomics, so the
+//    gradients are bit-reproducible.
+
+#include <math.h>
+
+#include "fa_device.h"
+#include "launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kNW = 4;     // waves per workgroup
+constexpr int kRows = 32;  // rows per wave and per streamed tile
+
+// LDS position (16-byte chunks) of chunk c of tile row r: the XOR pattern of
+// the forward kernel, conflict-free for 8-row column reads and for the
+// 4-row x 32-byte transposing reads.
+__device__ __forceinline__ int bswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <typename T>
+__device__ __forceinline__ float dot8_16(const u32x4_t& x, const u32x4_t& y) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (__is_same(T, __bf16)) {
+      s = __builtin_fmaf(lo_bf16(x[e]), lo_bf16(y[e]), s);
+      s = __builtin_fmaf(hi_bf16(x[e]), hi_bf16(y[e]), s);
+    } else {
+      const f16x2_t a = as_f16x2(x[e]), b = as_f16x2(y[e]);
+      s = __builtin_fmaf((float)a[0], (float)b[0], s);
+      s = __builtin_fmaf((float)a[1], (float)b[1], s);
+    }
+  }
+  return s;
+}
+
+// Two 32-row tiles (rows x D) staged global -> VGPRs -> LDS by the whole
+// workgroup: each thread moves kPer 16-byte chunks of each tile.
+template <typename T, int D>
+struct TilePair {
+  static constexpr int kCPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int kRB = D * 2;                       // bytes per row
+  static constexpr int kTileB = kRows * kRB;
+  static constexpr int kPer = kRows * kCPR / (kNW * 64);  // chunks per thread per tile
+  u32x4_t a[kPer], b[kPer];
+
+  // rows row0 .. row0+31 of the two tensors (token stride rs elements),
+  // rows >= nrows read as zero
+  __device__ __forceinline__ void load(const T* pa, const T* pb, size_t rs, int row0, int nrows,
+                                       int tid) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int p = tid + u * kNW * 64;
+      const int r = p / kCPR, c = p % kCPR;
+      const int row = row0 + r;
+      if (row < nrows) {
+        a[u] = *(const u32x4_t*)(pa + (size_t)row * rs + c * 8);
+        b[u] = *(const u32x4_t*)(pb + (size_t)row * rs + c * 8);
+      } else {
+        a[u] = u32x4_t{};
+        b[u] = u32x4_t{};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(FA_LDS(char)* ta, FA_LDS(char)* tb, int tid) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int p = tid + u * kNW * 64;
+      const int r = p / kCPR, c = p % kCPR;
+      const int pos = r * kRB + ((c ^ bswz(r)) * 16);
+      *(FA_LDS(u32x4_t)*)(ta + pos) = a[u];
+      *(FA_LDS(u32x4_t)*)(tb + pos) = b[u];
+    }
+  }
+};
+
+// Lane parts of the two LDS read patterns of a 32-row tile.
+template <int D>
+struct ReadLanes {
+  static constexpr int KS = D / 16, DB = D / 32, RB = D * 2;
+  int rowl[KS];  // 8 consecutive columns of row `col` (A operand, rows = MFMA rows)
+  int trl[DB];   // transposing read: columns of 32-wide block db, rows in P's order
+  __device__ __forceinline__ void init(int lane) {
+    const int col = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rowl[ks] = col * RB + ((ks * 2 + hh) ^ bswz(col)) * 16;
+    const int g = lane >> 4, ii = lane & 15, jj = ii >> 2, qq = ii & 3;
+    const int rr = 4 * hh + jj;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      const int ch = 4 * i + 2 * (g & 1) + (qq >> 1);
+      trl[i] = rr * RB + ((ch ^ bswz(rr)) * 16) + (qq & 1) * 8;
+    }
+  }
+};
+
+template <typename frag>
+__device__ __forceinline__ frag row_frag(const FA_LDS(char)* tile, int off) {
+  return *(const FA_LDS(frag)*)(tile + off);
+}
+
+// Transposing read: A operand whose k index follows the MFMA output row order
+// (rows 16t + 4hh + e and 16t + 8 + 4hh + e of the tile).
+template <typename frag>
+__device__ __forceinline__ frag tr_frag(const FA_LDS(char)* tile, int off, int t, int RB) {
+  const int base = off + 16 * t * RB;
+  s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS(s16x4_t)*)(tile + base));
+  s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS(s16x4_t)*)(tile + base + 8 * RB));
+  const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+  const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+  const u32x4_t u = {lo2.x, lo2.y, hi2.x, hi2.y};
+  return __builtin_bit_cast(frag, u);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// delta[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d]
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  const long long row = (long long)blockIdx.x * 256 + threadIdx.x;  // (b, i, h), h fastest
+  if (row >= (long long)a.B * a.Nq * a.H) return;
+  const int h = (int)(row % a.H);
+  const long long bi = row / a.H;
+  const int i = (int)(bi % a.Nq);
+  const int b = (int)(bi / a.Nq);
+  const u32x4_t* po = (const u32x4_t*)((const T*)a.o + row * D);
+  const u32x4_t* pd = (const u32x4_t*)((const T*)a.dout + row * D);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) s += dot8_16<T>(po[c], pd[c]);
+  a.delta[((long long)b * a.H + h) * a.Nq + i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: a workgroup per 128 keys of one (batch, head)
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using TP = TilePair<T, D>;
+  constexpr int KS = D / 16, DB = D / 32, TS = 2, RB = D * 2;
+  constexpr int kBufB = 2 * TP::kTileB + 2 * kRows * 4;  // Q, dO, lse, delta
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kBufB];
+  FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nbh = a.B * a.H;
+  const int kblk = blockIdx.x / nbh;  // ascending: causal key blocks with most queries first
+  const int bh = blockIdx.x - kblk * nbh;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int lq = a.Nq;
+  const int lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.Nk) : a.Nk;
+  const int off = lk - lq;
+  const int k0 = kblk * kNW * kRows;
+  const int kw0 = k0 + wave * kRows;  // this wave's first key
+  const int n = kw0 + col;             // this lane's key
+
+  const size_t rs = (size_t)a.H * D;
+  const T* qb = (const T*)a.q + (size_t)b * a.Nq * rs + (size_t)h * D;
+  const T* dob = (const T*)a.dout + (size_t)b * a.Nq * rs + (size_t)h * D;
+  const float* lseb = a.lse + ((size_t)b * a.H + h) * a.Nq;
+  const float* dlb = a.delta + ((size_t)b * a.H + h) * a.Nq;
+
+  // K and V rows of this lane's key (B operands), zero past the real keys
+  frag kf[KS], vf[KS];
+  {
+    const bool ok = n < lk;
+    const T* kr = (const T*)a.k + ((size_t)b * a.Nk + (ok ? n : 0)) * rs + (size_t)h * D;
+    const T* vr = (const T*)a.v + ((size_t)b * a.Nk + (ok ? n : 0)) * rs + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      kf[ks] = ok ? *(const frag*)(kr + ks * 16 + hh * 8) : z;
+      vf[ks] = ok ? *(const frag*)(vr + ks * 16 + hh * 8) : z;
+    }
+  }
+  f32x16_t dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16_t{};
+
+  // query chunks that see any key of the workgroup (causal: i >= k0 - off)
+  const int nch = (lq + kRows - 1) / kRows;
+  int c_begin = 0, c_wave = 0;
+  if (CAUSAL) {
+    c_begin = max(0, k0 - off) / kRows;
+    c_wave = max(0, kw0 - off) / kRows;
+  }
+  const bool wave_live = kw0 < lk;
+
+  ReadLanes<D> rl;
+  rl.init(lane);
+  TP st;
+  float st_l = 0.f;  // thread < 64: one lse (tid < 32) or delta (32 <= tid < 64) value
+  auto stage_load = [&](int c) {
+    st.load(qb, dob, rs, c * kRows, lq, tid);
+    if (tid < 2 * kRows) {
+      const int i = c * kRows + (tid & 31);
+      if (tid < kRows) {
+        // exp2 offset of row i; +inf for rows past the end or with no visible
+        // key (their probabilities are 0)
+        const float l = i < lq ? lseb[i] : -INFINITY;
+        st_l = l == -INFINITY ? INFINITY : l * kLog2e;
+      } else {
+        st_l = i < lq ? dlb[i] : 0.f;
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    FA_LDS(char)* base = smem + buf * kBufB;
+    st.store(base, base + TP::kTileB, tid);
+    if (tid < 2 * kRows) *(FA_LDS(float)*)(base + 2 * TP::kTileB + tid * 4) = st_l;
+  };
+
+  auto compute = [&](int c, int buf) {
+    const FA_LDS(char)* base = smem + buf * kBufB;
+    const FA_LDS(char)* tq = base;
+    const FA_LDS(char)* tdo = base + TP::kTileB;
+    const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * TP::kTileB);
+    const int q0 = c * kRows;
+    // S = Q K^T and dP = dO V^T: rows (queries) along registers, lanes = keys
+    f32x16_t s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mma(row_frag<frag>(tq, rl.rowl[ks]), kf[ks], s);
+      dp = mma(row_frag<frag>(tdo, rl.rowl[ks]), vf[ks], dp);
+    }
+    // register r holds query row 8*(r>>2) + 4*hh + (r&3) of the chunk
+    float lr[16], dr[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+      const f32x4_t l4 = *(const FA_LDS(f32x4_t)*)(tl + 8 * g + 4 * hh);
+      const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tl + kRows + 8 * g + 4 * hh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lr[4 * g + e] = l4[e];
+        dr[4 * g + e] = d4[e];
+      }
+    }
+    const bool masked = (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > q0 + off);
+    // query row m of the chunk sees this lane's key iff m >= lim (and the key is real)
+    const int lim = n - q0 - off - 4 * hh;
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = fast_exp2(__builtin_fmaf(s[r], a.c, -lr[r]));
+      if (masked) {
+        const int cr = 8 * (r >> 2) + (r & 3);
+        const bool vis = (n < lk) && (!CAUSAL || cr >= lim);
+        p[r] = vis ? p[r] : 0.f;
+      }
+      ds[r] = p[r] * (dp[r] - dr[r]);
+    }
+    frag pk[TS], dk[TS];
+#pragma unroll
+    for (int t = 0; t < TS; ++t) {
+      u32x4_t up, ud;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        up[e] = pack2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1], (T*)nullptr);
+        ud[e] = pack2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1], (T*)nullptr);
+      }
+      pk[t] = __builtin_bit_cast(frag, up);
+      dk[t] = __builtin_bit_cast(frag, ud);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (queries as the contraction index)
+#pragma unroll
+    for (int t = 0; t < TS; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dva[db] = mma(tr_frag<frag>(tdo, rl.trl[db], t, RB), pk[t], dva[db]);
+        dka[db] = mma(tr_frag<frag>(tq, rl.trl[db], t, RB), dk[t], dka[db]);
+      }
+  };
+
+  if (c_begin < nch) {
+    stage_load(c_begin);
+    stage_store(0);
+  }
+  __syncthreads();
+  if (c_begin + 1 < nch) stage_load(c_begin + 1);
+  for (int c = c_begin; c < nch; ++c) {
+    const int buf = (c - c_begin) & 1;
+    if (wave_live && c >= c_wave) compute(c, buf);
+    if (c + 1 < nch) stage_store(buf ^ 1);  // its last reader was step c-1
+    __syncthreads();
+    if (c + 2 < nch) stage_load(c + 2);
+  }
+
+  // dK = scale * dK^T, dV = dV^T for keys < Nk (padding keys: zero)
+  if (n < a.Nk) {
+    T* dkr = (T*)a.dk + ((size_t)b * a.Nk + n) * rs + (size_t)h * D;
+    T* dvr = (T*)a.dv + ((size_t)b * a.Nk + n) * rs + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * hh;
+        const f32x16_t& kk = dka[db];
+        const f32x16_t& vv = dva[db];
+        u32x2_t wk = {pack2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale, (T*)nullptr),
+                      pack2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale, (T*)nullptr)};
+        u32x2_t wv = {pack2(vv[4 * g4], vv[4 * g4 + 1], (T*)nullptr),
+                      pack2(vv[4 * g4 + 2], vv[4 * g4 + 3], (T*)nullptr)};
+        *(u32x2_t*)(dkr + d) = wk;
+        *(u32x2_t*)(dvr + d) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a workgroup per 128 query rows of one (batch, head)
+// ---------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using TP = TilePair<T, D>;
+  constexpr int KS = D / 16, DB = D / 32, TS = 2, RB = D * 2;
+  constexpr int kBufB = 2 * TP::kTileB;  // K, V
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kBufB];
+  FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nbh = a.B * a.H;
+  const int level = blockIdx.x / nbh;
+  const int bh = blockIdx.x - level * nbh;
+  const int qblk = CAUSAL ? (a.nqb - 1 - level) : level;  // causal: longest first
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int lq = a.Nq;
+  const int lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.Nk) : a.Nk;
+  const int off = lk - lq;
+  const int q0 = qblk * kNW * kRows;
+  const int wq0 = q0 + wave * kRows;
+  const int qi = wq0 + col;  // this lane's query row
+  const int wq_last = min(wq0 + kRows, lq) - 1;
+
+  const size_t rs = (size_t)a.H * D;
+  const T* kb = (const T*)a.k + (size_t)b * a.Nk * rs + (size_t)h * D;
+  const T* vb = (const T*)a.v + (size_t)b * a.Nk * rs + (size_t)h * D;
+
+  // Q and dO rows of this lane's query (B operands), lse and delta
+  frag qf[KS], dof[KS];
+  float lrow = INFINITY, drow = 0.f;
+  {
+    const bool ok = qi < lq;
+    const size_t ro = ((size_t)b * a.Nq + (ok ? qi : 0)) * rs + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      qf[ks] = ok ? *(const frag*)((const T*)a.q + ro + ks * 16 + hh * 8) : z;
+      dof[ks] = ok ? *(const frag*)((const T*)a.dout + ro + ks * 16 + hh * 8) : z;
+    }
+    if (ok) {
+      const float l = a.lse[((size_t)b * a.H + h) * a.Nq + qi];
+      lrow = l == -INFINITY ? INFINITY : l * kLog2e;
+      drow = a.delta[((size_t)b * a.H + h) * a.Nq + qi];
+    }
+  }
+  f32x16_t dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = f32x16_t{};
+
+  // key blocks of the workgroup and of this wave (causal: keys <= row + off)
+  int nkb = (lk + kRows - 1) / kRows, nkw = nkb;
+  if (CAUSAL) {
+    const int kmax = min(q0 + kNW * kRows, lq) - 1 + off;
+    nkb = kmax < 0 ? 0 : min(nkb, kmax / kRows + 1);
+    const int t = wq_last + off;
+    nkw = (wq_last < wq0 || t < 0) ? 0 : min(nkb, t / kRows + 1);
+  } else if (wq_last < wq0) {
+    nkw = 0;
+  }
+
+  ReadLanes<D> rl;
+  rl.init(lane);
+  TP st;
+  auto compute = [&](int j, int buf) {
+    const FA_LDS(char)* tk = smem + buf * kBufB;
+    const FA_LDS(char)* tv = tk + TP::kTileB;
+    const int k0 = j * kRows;
+    // S^T = K Q^T and dP^T = V dO^T: keys along registers, lanes = queries
+    f32x16_t s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mma(row_frag<frag>(tk, rl.rowl[ks]), qf[ks], s);
+      dp = mma(row_frag<frag>(tv, rl.rowl[ks]), dof[ks], dp);
+    }
+    const bool masked = (k0 + kRows > lk) || (CAUSAL && k0 + kRows - 1 > wq0 + off);
+    // key 8*(r>>2) + 4*hh + (r&3) of the block is visible iff that offset <= lim
+    const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;
+    const int lim = last - k0 - 4 * hh;
+    frag dsk[TS];
+#pragma unroll
+    for (int t = 0; t < TS; ++t) {
+      u32x4_t ud;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pr[2];
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const int r = 8 * t + 2 * e + z;
+          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lrow));
+          if (masked) p = (8 * (r >> 2) + (r & 3) <= lim) ? p : 0.f;
+          pr[z] = p * (dp[r] - drow);
+        }
+        ud[e] = pack2(pr[0], pr[1], (T*)nullptr);
+      }
+      dsk[t] = __builtin_bit_cast(frag, ud);
+    }
+    // dQ^T += K^T dS^T (keys as the contraction index)
+#pragma unroll
+    for (int t = 0; t < TS; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dqa[db] = mma(tr_frag<frag>(tk, rl.trl[db], t, RB), dsk[t], dqa[db]);
+  };
+
+  if (nkb > 0) {
+    st.load(kb, vb, rs, 0, lk, tid);
+    st.store(smem, smem + TP::kTileB, tid);
+  }
+  __syncthreads();
+  if (1 < nkb) st.load(kb, vb, rs, kRows, lk, tid);
+  for (int j = 0; j < nkb; ++j) {
+    const int buf = j & 1;
+    if (j < nkw) compute(j, buf);
+    if (j + 1 < nkb) {
+      FA_LDS(char)* nb = smem + (buf ^ 1) * kBufB;  // its last reader was step j-1
+      st.store(nb, nb + TP::kTileB, tid);
+    }
+    __syncthreads();
+    if (j + 2 < nkb) st.load(kb, vb, rs, (j + 2) * kRows, lk, tid);
+  }
+
+  if (qi < lq) {
+    T* dqr = (T*)a.dq + ((size_t)b * a.Nq + qi) * rs + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * hh;
+        const f32x16_t& x = dqa[db];
+        u32x2_t w = {pack2(x[4 * g4] * a.scale, x[4 * g4 + 1] * a.scale, (T*)nullptr),
+                     pack2(x[4 * g4 + 2] * a.scale, x[4 * g4 + 3] * a.scale, (T*)nullptr)};
+        *(u32x2_t*)(dqr + d) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t stream) {
+  // empty grids (no queries or no keys) are skipped: the other kernel still
+  // writes the zero gradients of its side
+  const long long rows = (long long)a.B * a.Nq * a.H;
+  if (rows > 0)
+    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned nbh = (unsigned)(a.B * a.H);
+  const unsigned gk = (unsigned)((a.Nk + kNW * kRows - 1) / (kNW * kRows)) * nbh;
+  const unsigned gq = (unsigned)a.nqb * nbh;
+  if (gk > 0) {
+    if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (gq > 0) {
+    if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+int bwd_block_rows() { return kNW * kRows; }
+
+hipError_t launch_bwd(const BwdArgs& a, fa_dtype_t dtype, int D, bool causal, hipStream_t stream) {
+  if (dtype == FA_BF16)
+    return D == 64 ? launch_bwd_td<__bf16, 64>(a, causal, stream) : launch_bwd_td<__bf16, 128>(a, causal, stream);
+  return D == 64 ? launch_bwd_td<_Float16, 64>(a, causal, stream) : launch_bwd_td<_Float16, 128>(a, causal, stream);
+}
+
+}  // namespace fa

@@ -76,4 +76,26 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, fa_dtype_t dtype, int D, hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;        // [B, H, Nq]
+  float* delta;            // workspace [B, H, Nq]: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* seqlens_k;
+  int B, H, Nq, Nk;
+  int nqb;                 // query blocks of bwd_block_rows() rows
+  float c;                 // scale * log2(e)
+  float scale;
+};
+
+int bwd_block_rows();
+// delta, then dK/dV, then dQ, all on `stream`
+hipError_t launch_bwd(const BwdArgs& a, fa_dtype_t dtype, int D, bool causal, hipStream_t stream);
+
 }  // namespace fa

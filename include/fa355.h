@@ -173,6 +173,30 @@ FA355_API fa_status_t fa_decode_splitkv_paged(const void* q, const void* k_pages
                               void* workspace, size_t workspace_bytes,
                               fa_dtype_t dtype, void* stream);
 
+/*
+ * Backward pass of fixed-length attention: the gradients dQ, dK, dV of a
+ * loss L given dO = dL/dO, for the forward pass fa_fwd computed (same q, k,
+ * v, scale, causal, seqlens_k; its o and lse).  The probabilities are
+ * recomputed from q, k and lse rather than stored (the recompute of the CSDN
+ * primer 轻松读懂FlashAttention 上, section Softmax求解重构):
+ *   dV = P^T dO,  dS = P o (dO V^T - rowsum(dO o O)),  dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ *   q, o, dout, dq: [B, Nq, H, D];  k, v, dk, dv: [B, Nk, H, D];  dtype fp16 or
+ *       bf16 (fp32: FA_ERR_UNSUPPORTED); dq, dk, dv written in that dtype
+ *   lse: [B, H, Nq] float32 from fa_fwd (rows with no visible key: -inf)
+ *   seqlens_k: as fa_fwd; padding keys (rows Lk .. Nk-1) get dk = dv = 0
+ *   workspace: device buffer of at least fa_bwd_workspace_bytes(B, H, Nq)
+ *       bytes (rowsum(dO o O), float32); contents on entry do not matter
+ * Three kernel launches on `stream` (row sums, then dK/dV, then dQ); no
+ * atomics, so the result is bit-reproducible.  The caller owns every buffer.
+ */
+FA355_API size_t fa_bwd_workspace_bytes(int B, int H, int Nq);
+FA355_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                             const int32_t* seqlens_k, void* workspace, size_t workspace_bytes,
+                             fa_dtype_t dtype, void* stream);
+
 /* Static strings; never NULL. */
 FA355_API const char* fa_status_string(fa_status_t status);
 FA355_API const char* fa_version(void);

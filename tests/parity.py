@@ -45,3 +45,37 @@ def assert_close(dtype, o_gpu, o_ref, lse_gpu=None, lse_ref=None, what=""):
         assert e["lse_inf_mismatch"] == 0, msg
         assert e["lse_max_abs"] <= LSE_TOL, msg
     return e
+
+
+# Gradients (backward pass).  The GPU rounds P and dS to the input dtype
+# before its MFMAs (relative error 2^-9 for bf16, 2^-12 for fp16 per element,
+# random in sign), on top of the rounding of dO and O in the row sums; the
+# result is compared by its relative RMS error and by its largest error
+# relative to the largest reference value.
+GRAD_TOL = {
+    "f16": dict(max_rel=1.5e-2, rel_rms=5e-3),
+    "bf16": dict(max_rel=3e-2, rel_rms=1e-2),
+}
+
+
+def grad_errors(g_gpu, g_ref):
+    g_gpu = np.asarray(g_gpu, dtype=np.float64)
+    g_ref = np.asarray(g_ref, dtype=np.float64)
+    d = g_gpu - g_ref
+    scale = max(float(np.max(np.abs(g_ref))) if g_ref.size else 0.0, 1e-30)
+    return {
+        "max_rel": float(np.max(np.abs(d))) / scale if d.size else 0.0,
+        "rel_rms": float(np.linalg.norm(d) / max(np.linalg.norm(g_ref), 1e-300)) if d.size else 0.0,
+        "nonfinite": int(np.count_nonzero(~np.isfinite(g_gpu))),
+    }
+
+
+def assert_grad_close(dtype, g_gpu, g_ref, what=""):
+    e = grad_errors(g_gpu, g_ref)
+    tol = GRAD_TOL[dtype]
+    msg = "%s %s: %s" % (what, dtype, e)
+    print("  ", msg, flush=True)
+    assert e["nonfinite"] == 0, msg
+    assert e["max_rel"] <= tol["max_rel"], msg
+    assert e["rel_rms"] <= tol["rel_rms"], msg
+    return e

@@ -26,6 +26,7 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
+        "fa_bwd", "fa_bwd_workspace_bytes",
         "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
@@ -184,3 +185,30 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     finally:
         monkeypatch.delenv("FA355_LIB")
         importlib.reload(fa)
+
+
+def test_bwd_validation():
+    """Argument checks of fa_bwd; all run before any HIP call."""
+    base = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=2, H=2, Nq=64, Nk=80, D=64,
+                scale=0.125, causal=1, sl=None, ws=P, wsb=1 << 20, dtype=fa.FA_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                         a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                         a["causal"], a["sl"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2560          # 600 floats, 256-byte rounded
+    assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED        # 16-bit only
+    assert call(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(B=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Nk=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert call(causal=3) == fa.FA_ERR_INVALID_ARG
+    assert call(do=None) == fa.FA_ERR_INVALID_ARG
+    assert call(dk=None) == fa.FA_ERR_INVALID_ARG
+    assert call(lse=MIS) == fa.FA_ERR_INVALID_ARG
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=fa.fa_bwd_workspace_bytes(2, 2, 64) - 1) == fa.FA_ERR_WORKSPACE
+    assert call(Nq=0, Nk=0) == fa.FA_OK                          # nothing to do, no device needed

@@ -1,0 +1,98 @@
+"""GPU parity of the backward pass (fa_bwd through the C ABI) against the oracle.
+
+The GPU backward consumes the GPU forward's o and lse (as a training step
+would); the oracle recomputes everything from q, k, v and dO.  Outputs are
+filled with NaN before each call, padding keys are NaN, and every case runs
+twice and must be bit-identical.
+"""
+
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import assert_grad_close
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def P(name, dtype, D, causal, B, H, Nq, Nk, seed, scale=None):
+    return wl.Workload(name, "prefill", dtype, H=H, D=D, causal=causal,
+                       scale=(1 / math.sqrt(D)) if scale is None else scale, seed=seed, B=B,
+                       Nq=Nq, Nk=Nk)
+
+
+def bwd_case(w, seqlens=None):
+    import exact_tiled_attention_11_amd as fa
+    fa.load()
+    q, k, v = wl.prefill_inputs(w)
+    do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D))
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            k[b, L:] = float("nan")
+            v[b, L:] = float("nan")
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    say("  fa_fwd %s" % w.name)
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, seqlens_k=sl)
+    outs = []
+    for rep in range(2):
+        dq = torch.full_like(qd, float("nan"))
+        dk = torch.full_like(kd, float("nan"))
+        dv = torch.full_like(vd, float("nan"))
+        say("  fa_bwd %s rep %d" % (w.name, rep))
+        fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, seqlens_k=sl, dq=dq,
+               dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+    dq, dk, dv = outs[0]
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            assert (dk[b, L:] == 0).all() and (dv[b, L:] == 0).all(), "padding keys get no gradient"
+    if w.Nk == 1 and not w.causal:
+        # One key: its probability is 1, so dS = dO.v - dO.o = 0 and the exact dQ
+        # and dK are zero; the GPU's only error is the rounding of o to the
+        # input dtype inside delta (relative 2^-8 per element) plus fp32 sums.
+        k64, v64, do64 = wl.to_f64(k), wl.to_f64(v), wl.to_f64(do)
+        bound = (w.scale * np.abs(k64).max() * np.abs(do64).sum(-1).max() * np.abs(v64).max()
+                 * 2.0 ** -7)
+        assert float(dq.abs().max()) <= bound and float(dk.abs().max()) <= bound, (
+            float(dq.abs().max()), float(dk.abs().max()), bound)
+        assert torch.equal(dv, do), "one key: dV = dO exactly"
+        return
+    rq, rk, rv = oracle.attention_bwd(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), wl.to_f64(do),
+                                      w.scale, w.causal, seqlens_k=seqlens)
+    assert_grad_close(w.dtype, wl.to_f64(dq), rq, "%s dq" % w.name)
+    assert_grad_close(w.dtype, wl.to_f64(dk), rk, "%s dk" % w.name)
+    assert_grad_close(w.dtype, wl.to_f64(dv), rv, "%s dv" % w.name)
+
+
+BWD = [
+    (P("bf16 D64 causal B2 H3 N300", "bf16", 64, True, 2, 3, 300, 300, 51), None),
+    (P("bf16 D64 noncausal B1 H2 Nq129 Nk200", "bf16", 64, False, 1, 2, 129, 200, 52), None),
+    (P("f16 D128 causal B1 H2 N257", "f16", 128, True, 1, 2, 257, 257, 53), None),
+    (P("bf16 D128 noncausal B2 H2 N160", "bf16", 128, False, 2, 2, 160, 160, 54), None),
+    (P("bf16 D64 causal Nq100 Nk300", "bf16", 64, True, 1, 2, 100, 300, 55), None),
+    (P("bf16 D64 causal Nq300 Nk100 (rows with no visible key)", "bf16", 64, True, 1, 2, 300, 100,
+       56), None),
+    (P("f16 D64 causal B2 H2 N300 padded keys", "f16", 64, True, 2, 2, 300, 300, 57), [300, 177]),
+    (P("bf16 D128 noncausal B1 H1 Nq1 Nk1", "bf16", 128, False, 1, 1, 1, 1, 58), None),
+    (P("f16 D64 causal B1 H4 N1000", "f16", 64, True, 1, 4, 1000, 1000, 59), None),
+]
+
+
+@pytest.mark.parametrize("w,seqlens", BWD, ids=lambda x: getattr(x, "name", str(x)))
+def test_bwd(w, seqlens):
+    bwd_case(w, seqlens)

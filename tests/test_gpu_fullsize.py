@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads as wl
-from parity import assert_close
+from parity import assert_close, assert_grad_close
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +183,31 @@ def test_decode_paged_full_size_sampled():
                                                    L, w.scale, False)
             assert_close(w.dtype, wl.to_f64(o_c[b, h])[None], o_ref, lse_c[b, h:h + 1].double().numpy(),
                          lse_ref, "%s b%d h%d" % (w.name, b, h))
+
+
+def test_bwd_full_size_heads():
+    """Gradients of the N8192 causal prefill, in the launch configuration
+    bench.py --config 9 times: two runs bit-identical, every gradient finite,
+    and three whole (batch, head) slices against the oracle's backward."""
+    fa = _fa()
+    w = wl.CFG[9]
+    say("generate %s" % w.name)
+    q, k, v = wl.prefill_inputs(w)
+    do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D))
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("fa_fwd + fa_bwd %s" % w.name)
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)
+    g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+        assert torch.isfinite(a).all().item()
+    dq, dk, dv = (t.cpu() for t in g1)
+    rng = np.random.default_rng(1009)
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        rq, rk, rv = oracle.attention_bwd(wl.to_f64(q[sl]), wl.to_f64(k[sl]), wl.to_f64(v[sl]),
+                                          wl.to_f64(do[sl]), w.scale, w.causal)
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref, "%s %s b%d h%d" % (w.name, name, b, h))

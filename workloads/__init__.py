@@ -64,6 +64,7 @@ class Workload:
     page_size: int = 0    # paged decode: rows per cache page
     prefix: int = 0       # prefill with the prefix mask: keys every query sees
     alibi: bool = False   # prefill with ALiBi: slopes of alibi_slopes(H)
+    backward: bool = False  # the gradients of the prefill (dQ, dK, dV from dO)
     lens_fixed: Optional[Sequence[int]] = field(default=None, compare=False)
 
     def lengths(self) -> np.ndarray:
@@ -79,8 +80,11 @@ class Workload:
         return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
 
     def flops(self) -> float:
-        """Algorithmic FLOPs: 4*D per visible (query, key) pair."""
-        return 4.0 * self.D * self.H * self.visible_pairs_per_head()
+        """Algorithmic FLOPs: 4*D per visible (query, key) pair for the forward
+        (S = Q K^T and P V); 10*D for the backward (S recomputed, dP = dO V^T,
+        dV = P^T dO, dQ = dS K, dK = dS^T Q)."""
+        per_pair = 10.0 if self.backward else 4.0
+        return per_pair * self.D * self.H * self.visible_pairs_per_head()
 
     def visible_pairs_per_head(self) -> int:
         if self.kind == "prefill":
@@ -135,6 +139,9 @@ CFG = {
 # 2048 keys bidirectional) and with ALiBi slopes.
 CFG[7] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 prefix 2048", prefix=2048)
 CFG[8] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 ALiBi", alibi=True)
+
+# Beyond the table: the gradients of the N8192 causal prefill.
+CFG[9] = replace(CFG[3], name="backward causal bf16 B4 H16 N8192 D64", backward=True)
 
 # Beyond the table: the decode workload over a paged cache (16-row pages at
 # shuffled pool positions), the cache layout of serving runtimes.
