@@ -17,6 +17,7 @@ from .exact import (  # noqa: F401
     alibi_bias,
     attention_rows,
     attention,
+    attention_dropout,
     attention_bwd,
     attention_varlen,
     decode,
@@ -25,3 +26,4 @@ from .exact import (  # noqa: F401
     merge,
     finalize,
 )
+from .dropout import philox4x32, drop_threshold, keep_mask, keep_scale  # noqa: F401,E402

@@ -29,18 +29,23 @@ the repository's design notes):
 
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against brute force in pure Python, closed forms, invariants and torch's CPU
-float64 attention (see that file).  ``partial``/``merge``/``finalize`` are
+float64 attention (see that file); the backward in
+``tests/test_oracle_bwd_pins.py`` and the dropout paths in
+``tests/test_oracle_dropout_pins.py``.  ``partial``/``merge``/``finalize`` are
 not used by ``attention``; they exist so the tests can check the pages'
 block-merge claim against the plain definition.
 """
 
 import numpy as np
 
+from . import dropout as _dropout
+
 __all__ = [
     "scores",
     "visible",
     "attention_rows",
     "attention",
+    "attention_dropout",
     "attention_varlen",
     "decode",
     "partial",
@@ -89,7 +94,8 @@ def alibi_bias(q_pos, lq, lk, slope):
     return -float(slope) * np.abs(j[None, :] - (q_pos[:, None] + (lk - lq))).astype(_F64)
 
 
-def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal, prefix=0, alibi_slope=None):
+def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal, prefix=0, alibi_slope=None,
+                   keep=None, keep_scale=1.0):
     """Output rows and log-sum-exp for a set of query rows of one (batch, head).
 
     q_rows: [n, D] query vectors; q_pos: [n] their row indices 0..lq-1;
@@ -100,6 +106,8 @@ def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal, prefix=0, alibi_s
     P V.  Rows are independent, so computing a subset of rows gives exactly
     the rows of the full result.  ``prefix`` and ``alibi_slope`` select the
     prefix mask and the ALiBi bias (see ``visible`` and ``alibi_bias``).
+    ``keep`` ([n, lk] bool) applies attention dropout: O = (P o keep) V *
+    keep_scale, with P (and so lse) the undropped softmax.
     """
     q_rows = np.asarray(q_rows, dtype=_F64)
     n, d = q_rows.shape
@@ -118,8 +126,9 @@ def attention_rows(q_rows, q_pos, k, v, lq, lk, scale, causal, prefix=0, alibi_s
     m_shift = np.where(empty, 0.0, m)
     p = np.exp(s - m_shift[:, None])                    # exp(-inf) = 0 for masked keys
     ell = p.sum(axis=1)                                 # softmax denominator
+    pv = p if keep is None else np.where(keep, p, 0.0) * float(keep_scale)
     with np.errstate(invalid="ignore", divide="ignore"):
-        o = (p @ vv) / ell[:, None]
+        o = (pv @ vv) / ell[:, None]
         lse = m + np.log(ell)
     o[empty] = 0.0
     lse[empty] = -np.inf
@@ -154,7 +163,36 @@ def attention(q, k, v, scale, causal, seqlens_k=None, row_chunk=1024, prefix=0,
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None):
+def attention_dropout(q, k, v, scale, causal, dropout_p, seed, seqlens_k=None, row_chunk=1024):
+    """Batched attention with attention dropout (BSHD layout), the form the
+    HF integration guide's parameter table gives for training: dropout_p is
+    the probability of dropping a weight.  The keep decisions and their
+    scale are those of ``oracle.dropout`` (Philox4x32-10 counters per
+    (batch, head, query, 16-key group)).  Returns O [B, Nq, H, D] and the
+    undropped lse [B, H, Nq].
+    """
+    q = np.asarray(q)
+    B, nq, H, D = q.shape
+    nk = k.shape[1]
+    t = _dropout.drop_threshold(dropout_p)
+    o = np.zeros((B, nq, H, v.shape[-1]), _F64)
+    lse = np.zeros((B, H, nq), _F64)
+    for b in range(B):
+        lk = nk if seqlens_k is None else int(seqlens_k[b])
+        for h in range(H):
+            for r0 in range(0, nq, row_chunk):
+                r1 = min(nq, r0 + row_chunk)
+                rows = np.arange(r0, r1)
+                keep = _dropout.keep_mask(seed, b, h, rows, lk, t)
+                ob, lb = attention_rows(q[b, r0:r1, h, :], rows, k[b, :, h, :], v[b, :, h, :],
+                                        nq, lk, scale, causal, keep=keep,
+                                        keep_scale=_dropout.keep_scale(t))
+                o[b, r0:r1, h, :] = ob
+                lse[b, h, r0:r1] = lb
+    return o, lse
+
+
+def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, seed=0):
     """Gradients of the forward definition: given dO = dL/dO, returns
     (dQ, dK, dV) in the BSHD layout, float64.
 
@@ -167,6 +205,9 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None):
       dQ = scale dS K;  dK = scale dSᵀ Q.
     Masked pairs have P = 0 and so no gradient; keys >= Lk (padding) get
     dK = dV = 0; a row with no visible key contributes nothing.
+    With dropout (``oracle.dropout``), O = (P o Z) V with Z = keep * scale;
+    then dV = (P o Z)ᵀ dO, dP = (dO Vᵀ) o Z, and the rest is unchanged
+    (rowsum(dO o O) still equals rowsum(P o dP)).
     """
     q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
     B, nq, H, D = q.shape
@@ -191,9 +232,14 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None):
             e = np.exp(s - m_shift[:, None])
             ell = e.sum(axis=1)
             p = np.where(ell[:, None] > 0, e / np.where(ell > 0, ell, 1.0)[:, None], 0.0)
-            o = p @ vv
-            dv[b, :lk, h] = p.T @ g
-            dp = g @ vv.T
+            if dropout_p:
+                t = _dropout.drop_threshold(dropout_p)
+                z = _dropout.keep_mask(seed, b, h, np.arange(nq), lk, t) * _dropout.keep_scale(t)
+            else:
+                z = np.ones_like(p)
+            o = (p * z) @ vv
+            dv[b, :lk, h] = (p * z).T @ g
+            dp = (g @ vv.T) * z
             delta = (g * o).sum(axis=1)
             ds = p * (dp - delta[:, None])
             dq[b, :, h] = float(scale) * (ds @ kk)
