@@ -26,9 +26,11 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
-    "fa_fwd", "fa_fwd_masked", "fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
+    "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout",
+    "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
-    "fwd", "fwd_masked", "bwd", "fwd_varlen", "decode_splitkv", "decode_splitkv_paged",
+    "fwd", "fwd_masked", "fwd_dropout", "bwd", "fwd_varlen", "decode_splitkv",
+    "decode_splitkv_paged",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -38,10 +40,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_u64 = ctypes.c_uint64
 _SIGS = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp]),
     "fa_fwd_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _i,
                            _vp]),
+    "fa_fwd_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _f, _u64,
+                            _i, _vp]),
+    "fa_bwd_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                            _i, _vp, _f, _u64, _vp, _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _vp, _sz, _i, _vp]),
@@ -99,6 +106,19 @@ def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, pr
                   dtype, stream) -> int:
     return load().fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
                                 alibi_slopes, dtype, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, dropout_p, seed,
+                   dtype, stream) -> int:
+    return load().fa_fwd_dropout(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k,
+                                 dropout_p, seed, dtype, stream)
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k,
+                   dropout_p, seed, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal,
+                                 seqlens_k, dropout_p, seed, workspace, workspace_bytes, dtype,
+                                 stream)
 
 
 def fa_bwd_workspace_bytes(B, H, Nq) -> int:
@@ -230,9 +250,35 @@ def fwd_masked(q, k, v, *, causal: bool = False, scale: Optional[float] = None, 
     return out, lse
 
 
+def fwd_dropout(q, k, v, *, dropout_p: float, seed: int, causal: bool = False,
+                scale: Optional[float] = None, seqlens_k=None, out=None, lse=None,
+                return_lse: bool = True, stream=None) -> Tuple:
+    """fwd with attention dropout (training): keep decisions from Philox4x32-10 keyed by seed."""
+    import torch
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
+        raise ValueError("seqlens_k must be int32[B]")
+    st = fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D,
+                        float(scale), int(bool(causal)), _ptr(seqlens_k), float(dropout_p),
+                        int(seed) & 0xFFFFFFFFFFFFFFFF, _dtype_code(q), _stream(stream))
+    _check("fa_fwd_dropout", st)
+    return out, lse
+
+
 def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
-        seqlens_k=None, dq=None, dk=None, dv=None, workspace=None, stream=None) -> Tuple:
-    """Gradients (dq, dk, dv) for the forward fwd(q, k, v) that produced o and lse, given dout."""
+        seqlens_k=None, dropout_p: float = 0.0, seed: int = 0, dq=None, dk=None, dv=None,
+        workspace=None, stream=None) -> Tuple:
+    """Gradients (dq, dk, dv) for the forward fwd(q, k, v) that produced o and lse, given dout
+    (with dropout_p > 0: for fwd_dropout with the same dropout_p and seed)."""
     import torch
     B, Nq, H, D = q.shape
     Nk = k.shape[1]
@@ -244,6 +290,13 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] =
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
                                 device=q.device)
+    if dropout_p:
+        st = fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                            _ptr(seqlens_k), float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                            _ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
+        _check("fa_bwd_dropout", st)
+        return dq, dk, dv
     st = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                 _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)), _ptr(seqlens_k),
                 _ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))

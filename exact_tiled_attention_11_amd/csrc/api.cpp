@@ -48,6 +48,73 @@ fa_status_t from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP
 
 constexpr float kLog2eF = 1.4426950408889634f;
 
+// Dropout probability -> byte threshold t = round(256 p) (at most 255); the
+// kept weights are scaled by 256 / (256 - t).
+bool drop_threshold(float p, uint32_t& t, float& scale) {
+  if (!(p >= 0.f && p < 1.f)) return false;
+  const double x = floor((double)p * 256.0 + 0.5);
+  t = x > 255.0 ? 255u : (uint32_t)x;
+  scale = (float)(256.0 / (256.0 - (double)t));
+  return true;
+}
+
+// Fixed-length prefill with the optional mask families and dropout.
+fa_status_t fwd_fixed(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Nq, int Nk, int D, float scale, int causal,
+                      const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
+                      uint32_t drop_t, float drop_scale, uint64_t seed, fa_dtype_t dtype,
+                      void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  // the mask families and dropout are implemented by the 16-bit kernel only
+  if (dtype == FA_F32 && (prefix != 0 || alibi_slopes || drop_t)) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if ((causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  if (prefix < 0 || (prefix > 0 && !causal)) return FA_ERR_INVALID_ARG;
+  if (Nq == 0) return FA_OK;
+  if (!q || !o || ((!k || !v) && Nk > 0)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(seqlens_k) || ((uintptr_t)alibi_slopes & 3u) != 0)
+    return FA_ERR_INVALID_ARG;
+  // element offsets must fit the kernels' 64-bit address math and grid limits
+  const int rows = fa::fwd_block_rows(dtype, D);
+  const long long nqb = ((long long)Nq + rows - 1) / rows;
+  const long long grid = nqb * B * H;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)B * Nq > 0x7fffffffLL || (long long)B * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+
+  fa_status_t st = device_ok();
+  if (st != FA_OK) return st;
+
+  fa::FwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.seqlens_k = seqlens_k;
+  a.B = B;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.nqb = (int)nqb;
+  a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
+  a.prefix = prefix;
+  a.alibi = alibi_slopes;
+  a.drop_t = drop_t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_scale = drop_scale;
+  return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, false, (unsigned)grid,
+                                 (hipStream_t)stream));
+}
+
+fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                     int D, float scale, int causal, const int32_t* seqlens_k, uint32_t drop_t,
+                     float drop_scale, uint64_t seed, void* workspace, size_t workspace_bytes,
+                     fa_dtype_t dtype, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -69,46 +136,19 @@ fa_status_t fa_fwd_masked(const void* q, const void* k, const void* v, void* o, 
                           int B, int H, int Nq, int Nk, int D, float scale, int causal,
                           const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
                           fa_dtype_t dtype, void* stream) {
-  if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
-  // the mask families are implemented by the 16-bit kernel only
-  if (dtype == FA_F32 && (prefix != 0 || alibi_slopes)) return FA_ERR_UNSUPPORTED;
-  if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
-  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-  if ((causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
-  if (prefix < 0 || (prefix > 0 && !causal)) return FA_ERR_INVALID_ARG;
-  if (Nq == 0) return FA_OK;
-  if (!q || !o || ((!k || !v) && Nk > 0)) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(seqlens_k) || ((uintptr_t)alibi_slopes & 3u) != 0)
-    return FA_ERR_INVALID_ARG;
-  // element offsets must fit the kernels' 64-bit address math and grid limits
-  const int rows = fa::fwd_block_rows(dtype, D);
-  const long long nqb = ((long long)Nq + rows - 1) / rows;
-  const long long grid = nqb * B * H;
-  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  if ((long long)B * Nq > 0x7fffffffLL || (long long)B * Nk > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  (void)esize;
+  return fwd_fixed(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
+                   alibi_slopes, 0u, 1.f, 0u, dtype, stream);
+}
 
-  fa_status_t st = device_ok();
-  if (st != FA_OK) return st;
-
-  fa::FwdArgs a = {};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.seqlens_k = seqlens_k;
-  a.B = B;
-  a.H = H;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.nqb = (int)nqb;
-  a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
-  a.prefix = prefix;
-  a.alibi = alibi_slopes;
-  return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, false, (unsigned)grid,
-                                 (hipStream_t)stream));
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                           const int32_t* seqlens_k, float dropout_p, uint64_t seed,
+                           fa_dtype_t dtype, void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return fwd_fixed(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, 0, nullptr, t, sc,
+                   seed, dtype, stream);
 }
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -128,6 +168,32 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                    int D, float scale, int causal, const int32_t* seqlens_k, void* workspace,
                    size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, 0u,
+                  1.f, 0u, workspace, workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                           const int32_t* seqlens_k, float dropout_p, uint64_t seed,
+                           void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                           void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, t,
+                  sc, seed, workspace, workspace_bytes, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                     int D, float scale, int causal, const int32_t* seqlens_k, uint32_t drop_t,
+                     float drop_scale, uint64_t seed, void* workspace, size_t workspace_bytes,
+                     fa_dtype_t dtype, void* stream) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit only
   if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
@@ -171,8 +237,16 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   a.nqb = (int)((Nq + rows - 1) / rows);
   a.c = fmaxf(scale * kLog2eF, 1e-30f);  // the forward's exponent scale
   a.scale = scale;
+  a.drop_t = drop_t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_scale = drop_scale;
   return from_hip(fa::launch_bwd(a, dtype, D, causal != 0, (hipStream_t)stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
   if (nseq < 1 || total_q < 0) return 0;

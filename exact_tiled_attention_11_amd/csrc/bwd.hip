@@ -26,6 +26,12 @@
 //  * Tiles are staged through VGPRs with ordinary loads (the compiler counts
 //    the waits); every result is written once, with no atomics, so the
 //    gradients are bit-reproducible.
+//  * Dropout (the forward's keep decisions, redrawn from the same Philox
+//    counters): with Z = keep / (1 - p), dV = (P o Z)^T dO and
+//    dS = P o (dP o Z - delta).  The dQ kernel has the forward's lane layout
+//    and draws the words the same way; in the dK/dV kernel lanes are keys,
+//    so each lane draws the call of one query row and the bytes are
+//    transposed through a small LDS tile of the wave.
 
 #include <math.h>
 
@@ -163,7 +169,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV: a workgroup per 128 keys of one (batch, head)
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+// LDS bytes per wave of the keep-byte transpose: 32 keys x 32 queries, rows
+// padded to 36 bytes
+constexpr int kTrRow = 36;
+constexpr int kTrWave = 32 * kTrRow;
+
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -173,9 +184,11 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * kBufB];
   FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
+  __shared__ __attribute__((aligned(16))) char trbuf_raw[DROP ? kNW * kTrWave : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  FA_LDS(uint8_t)* trb = (FA_LDS(uint8_t)*)trbuf_raw + (DROP ? wave * kTrWave : 0);
 
   const int nbh = a.B * a.H;
   const int kblk = blockIdx.x / nbh;  // ascending: causal key blocks with most queries first
@@ -273,7 +286,21 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
     const bool masked = (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > q0 + off);
     // query row m of the chunk sees this lane's key iff m >= lim (and the key is real)
     const int lim = n - q0 - off - 4 * hh;
-    float p[16], ds[16];
+    uint32_t kw[4];
+    if constexpr (DROP) {
+      // this lane draws the bytes of keys kw0 + 16*hh .. +15 for query q0 + col
+      // and stores them at [key][query]; then reads the bytes of its own key
+      // for its queries 8g + 4hh .. +3 (word g of register group g)
+      const Philox4 x = philox4x32_10((uint32_t)((kw0 >> 4) + hh), (uint32_t)(q0 + col),
+                                      (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        trb[(16 * hh + m) * kTrRow + col] = (uint8_t)(x.w[m >> 2] >> (8 * (m & 3)));
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        kw[g] = *(const FA_LDS(uint32_t)*)(trb + col * kTrRow + 8 * g + 4 * hh);
+    }
+    float p[16], pd[16], ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       p[r] = fast_exp2(__builtin_fmaf(s[r], a.c, -lr[r]));
@@ -282,7 +309,14 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
         const bool vis = (n < lk) && (!CAUSAL || cr >= lim);
         p[r] = vis ? p[r] : 0.f;
       }
-      ds[r] = p[r] * (dp[r] - dr[r]);
+      if constexpr (DROP) {
+        const bool kp = kept(kw[r >> 2], r & 3, a.drop_t);
+        pd[r] = kp ? p[r] : 0.f;
+        ds[r] = p[r] * ((kp ? dp[r] * a.drop_scale : 0.f) - dr[r]);
+      } else {
+        pd[r] = p[r];
+        ds[r] = p[r] * (dp[r] - dr[r]);
+      }
     }
     frag pk[TS], dk[TS];
 #pragma unroll
@@ -290,7 +324,7 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
       u32x4_t up, ud;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        up[e] = pack2(p[8 * t + 2 * e], p[8 * t + 2 * e + 1], (T*)nullptr);
+        up[e] = pack2(pd[8 * t + 2 * e], pd[8 * t + 2 * e + 1], (T*)nullptr);
         ud[e] = pack2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1], (T*)nullptr);
       }
       pk[t] = __builtin_bit_cast(frag, up);
@@ -320,7 +354,9 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
     if (c + 2 < nch) stage_load(c + 2);
   }
 
-  // dK = scale * dK^T, dV = dV^T for keys < Nk (padding keys: zero)
+  // dK = scale * dK^T, dV = dV^T (times 1 / (1 - p) with dropout) for keys
+  // < Nk (padding keys: zero)
+  const float vsc = DROP ? a.drop_scale : 1.f;
   if (n < a.Nk) {
     T* dkr = (T*)a.dk + ((size_t)b * a.Nk + n) * rs + (size_t)h * D;
     T* dvr = (T*)a.dv + ((size_t)b * a.Nk + n) * rs + (size_t)h * D;
@@ -333,8 +369,8 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
         const f32x16_t& vv = dva[db];
         u32x2_t wk = {pack2(kk[4 * g4] * a.scale, kk[4 * g4 + 1] * a.scale, (T*)nullptr),
                       pack2(kk[4 * g4 + 2] * a.scale, kk[4 * g4 + 3] * a.scale, (T*)nullptr)};
-        u32x2_t wv = {pack2(vv[4 * g4], vv[4 * g4 + 1], (T*)nullptr),
-                      pack2(vv[4 * g4 + 2], vv[4 * g4 + 3], (T*)nullptr)};
+        u32x2_t wv = {pack2(vv[4 * g4] * vsc, vv[4 * g4 + 1] * vsc, (T*)nullptr),
+                      pack2(vv[4 * g4 + 2] * vsc, vv[4 * g4 + 3] * vsc, (T*)nullptr)};
         *(u32x2_t*)(dkr + d) = wk;
         *(u32x2_t*)(dvr + d) = wv;
       }
@@ -344,7 +380,7 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 // ---------------------------------------------------------------------------
 // dQ: a workgroup per 128 query rows of one (batch, head)
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -426,6 +462,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     // key 8*(r>>2) + 4*hh + (r&3) of the block is visible iff that offset <= lim
     const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;
     const int lim = last - k0 - 4 * hh;
+    uint32_t kw[4];
+    if constexpr (DROP) keep_words_rows(kw, k0 >> 4, hh, qi, h, b, a.seed_lo, a.seed_hi);
     frag dsk[TS];
 #pragma unroll
     for (int t = 0; t < TS; ++t) {
@@ -438,7 +476,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
           const int r = 8 * t + 2 * e + z;
           float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lrow));
           if (masked) p = (8 * (r >> 2) + (r & 3) <= lim) ? p : 0.f;
-          pr[z] = p * (dp[r] - drow);
+          if constexpr (DROP)
+            pr[z] = p * ((kept(kw[r >> 2], r & 3, a.drop_t) ? dp[r] * a.drop_scale : 0.f) - drow);
+          else
+            pr[z] = p * (dp[r] - drow);
         }
         ud[e] = pack2(pr[0], pr[1], (T*)nullptr);
       }
@@ -499,14 +540,25 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
   const unsigned nbh = (unsigned)(a.B * a.H);
   const unsigned gk = (unsigned)((a.Nk + kNW * kRows - 1) / (kNW * kRows)) * nbh;
   const unsigned gq = (unsigned)a.nqb * nbh;
+  const bool drop = a.drop_t != 0;
   if (gk > 0) {
-    if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), dim3(gk), dim3(kNW * 64), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+    if (drop) {
+      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+    } else {
+      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (gq > 0) {
-    if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), dim3(gq), dim3(kNW * 64), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+    if (drop) {
+      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+    } else {
+      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -97,4 +97,66 @@ __device__ __forceinline__ f16x2_t as_f16x2(unsigned w) { return __builtin_bit_c
 __device__ __forceinline__ float lo_bf16(unsigned u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
 
+// ---------------------------------------------------------------------------
+// Attention dropout: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// Random Numbers: As Easy as 1, 2, 3", SC 2011).  A round multiplies words 0
+// and 2 by the two Philox multipliers; the new words are (hi(M1*x2) ^ x1 ^
+// k0, lo(M1*x2), hi(M0*x0) ^ x3 ^ k1, lo(M0*x0)); the key advances by the two
+// Weyl constants after each round.  Ten rounds.
+//
+// Keep decisions: pair (query i, key j) of batch b and head h takes byte
+// (j mod 4) of word ((j / 4) mod 4) of Philox(counter (j / 16, i, h, b), key
+// (seed low, seed high)), least significant byte first, and is kept iff the
+// byte is >= t = round(256 p).
+// ---------------------------------------------------------------------------
+struct Philox4 {
+  uint32_t w[4];
+};
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+// The value lane l^32 holds (v_permlane32_swap returns the lane's own value
+// in one result and its partner's in the other; equal values are the same
+// either way).
+__device__ __forceinline__ uint32_t partner32(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] == x ? r[1] : r[0];
+}
+
+// Keep words of one 32-key block for a lane whose MFMA registers r hold keys
+// 8*(r>>2) + 4*hh + (r&3) of the block (lanes = queries, row i): lanes with
+// hh = 0 draw the block's first 16-key group, hh = 1 the second, and the
+// halves trade the words the other needs.  Word g serves registers 4g..4g+3
+// (byte r&3).
+__device__ __forceinline__ void keep_words_rows(uint32_t kw[4], int group0, int hh, int i, int h,
+                                                int b, uint32_t s0, uint32_t s1) {
+  const Philox4 x = philox4x32_10((uint32_t)(group0 + hh), (uint32_t)i, (uint32_t)h, (uint32_t)b, s0, s1);
+  const uint32_t send0 = hh ? x.w[0] : x.w[1];
+  const uint32_t send1 = hh ? x.w[2] : x.w[3];
+  const uint32_t got0 = partner32(send0), got1 = partner32(send1);
+  kw[0] = hh ? got0 : x.w[0];
+  kw[1] = hh ? got1 : x.w[2];
+  kw[2] = hh ? x.w[1] : got0;
+  kw[3] = hh ? x.w[3] : got1;
+}
+
+__device__ __forceinline__ bool kept(uint32_t word, int byte, uint32_t t) {
+  return ((word >> (8 * byte)) & 0xffu) >= t;
+}
+
 }  // namespace fa

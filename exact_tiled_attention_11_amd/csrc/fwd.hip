@@ -119,7 +119,7 @@ __device__ __forceinline__ u32x4_t make_rsrc(const char* base, unsigned bytes) {
 // longest first; varlen grids read the sorted tile list of the schedule
 // kernel and may hold more workgroups than tiles (then false).
 struct WorkItem {
-  int h, qblk, lq, lk;
+  int b, h, qblk, lq, lk;
   long long q_tok0, k_tok0, lse_base;
 };
 template <bool CAUSAL, bool VARLEN>
@@ -130,6 +130,7 @@ __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
     const int bh = blockIdx.x - level * nbh;
     w.qblk = CAUSAL ? (a.nqb - 1 - level) : level;
     const int b = bh / a.H;
+    w.b = b;
     w.h = bh - b * a.H;
     w.lq = a.Nq;
     w.lk = a.Nk;
@@ -139,6 +140,7 @@ __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
     w.lse_base = ((long long)b * a.H + w.h) * a.Nq;
   } else {
     const int t = blockIdx.x / a.H;
+    w.b = 0;
     w.h = blockIdx.x - t * a.H;
     if (t >= a.sched[0]) return false;
     const int* tl = a.sched + 2 + 4 * a.nseq + 2 * t;
@@ -550,8 +552,14 @@ struct PipeCfg {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN, bool ALIBI>
+// MODE: kPipePlain, kPipeAlibi (ALiBi bias) or kPipeDrop (attention dropout);
+// the last two are fixed-length only.
+constexpr int kPipePlain = 0, kPipeAlibi = 1, kPipeDrop = 2;
+
+template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN, int MODE>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdArgs a) {
+  constexpr bool ALIBI = MODE == kPipeAlibi;
+  constexpr bool DROP = MODE == kPipeDrop;
   using C = PipeCfg<T, D, NW, PK>;
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -713,6 +721,17 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sS = mma(kfrag(IC<0>{}, ks), qf[ks], ks == 0 ? f32x16_t{} : sS);
   };
+  // Dropout: keep words of the current block (word g: registers 4g..4g+3).
+  // The row sums take every probability; the P V operand only the kept ones
+  // (their 1 / (1 - p) is applied to O at the end).
+  uint32_t kw[4] = {0u, 0u, 0u, 0u};
+  auto drop2 = [&](int c, float& p0, float& p1) __attribute__((always_inline)) {
+    if constexpr (DROP) {
+      const uint32_t w = kw[c >> 1];
+      p0 = kept(w, 2 * (c & 1), a.drop_t) ? p0 : 0.f;
+      p1 = kept(w, 2 * (c & 1) + 1, a.drop_t) ? p1 : 0.f;
+    }
+  };
   // probabilities exp2(sX) into pk; returns this lane's sum
   auto probs = [&]() __attribute__((always_inline)) -> float {
     float ts = 0.f;
@@ -721,10 +740,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
       u32x4_t w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(sX[8 * t + 2 * e]);
-        const float p1 = fast_exp2(sX[8 * t + 2 * e + 1]);
+        float p0 = fast_exp2(sX[8 * t + 2 * e]);
+        float p1 = fast_exp2(sX[8 * t + 2 * e + 1]);
         ts += p0;
         ts += p1;
+        drop2(4 * t + e, p0, p1);
         w[e] = pack2(p0, p1, (T*)nullptr);
       }
       pk[t] = __builtin_bit_cast(frag, w);
@@ -770,6 +790,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // copies of it would not fit the register budget.
   auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
+    if constexpr (DROP) keep_words_rows(kw, 2 * u, hh, wq0 + col, wi.h, wi.b, a.seed_lo, a.seed_hi);
     const float ms = mrow == -INFINITY ? 0.f : mrow;
     // ALiBi: -slope * |key - position| in exp2 units, key 8*(r>>2) + 4*hh +
     // (r&3) of the block, position qi + off.  In a causal block left of the
@@ -828,8 +849,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     auto acc2 = [&](int c) __attribute__((always_inline)) {
       ts += pe[2 * c];
       ts += pe[2 * c + 1];
+      float p0 = pe[2 * c], p1 = pe[2 * c + 1];
+      drop2(c, p0, p1);
       u32x4_t w = __builtin_bit_cast(u32x4_t, pk[c >> 2]);
-      w[c & 3] = pack2(pe[2 * c], pe[2 * c + 1], (T*)nullptr);
+      w[c & 3] = pack2(p0, p1, (T*)nullptr);
       pk[c >> 2] = __builtin_bit_cast(frag, w);
     };
     // pair p: exp2 in chunk p*RP, add and pack in chunk p*RP + ALAG; the
@@ -883,7 +906,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   const float lt = half_sum(lrow);
   const int qi = wq0 + col;
   if (qi < lq) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if constexpr (DROP) inv *= a.drop_scale;
     T* orow = (T*)a.o + (size_t)(wi.q_tok0 + qi) * rs + (size_t)wi.h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -1040,16 +1064,21 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
   if constexpr (UsePipe<T, D>::value) {
     constexpr int NW = 4, PK = FA_PIPE_PK;
     constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
+    constexpr int P0 = kPipePlain, PA = kPipeAlibi, PD = kPipeDrop;
     if (a.alibi) {  // fixed-length only (the entry point checks)
-      if (causal) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, true>, grid, NW * 64, lds, stream, a);
-      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, true>, grid, NW * 64, lds, stream, a);
+      if (causal) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PA>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, PA>, grid, NW * 64, lds, stream, a);
+    }
+    if (a.drop_t) {  // fixed-length only (the entry point checks)
+      if (causal) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PD>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, PD>, grid, NW * 64, lds, stream, a);
     }
     if (causal) {
-      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, false>, grid, NW * 64, lds, stream, a);
-      return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, false>, grid, NW * 64, lds, stream, a);
+      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, P0>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, P0>, grid, NW * 64, lds, stream, a);
     }
-    if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, false>, grid, NW * 64, lds, stream, a);
-    return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, false>, grid, NW * 64, lds, stream, a);
+    if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, P0>, grid, NW * 64, lds, stream, a);
+    return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, P0>, grid, NW * 64, lds, stream, a);
   }
   using Tl = Tile<T, D>;
   constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;

@@ -27,6 +27,10 @@ struct FwdArgs {
   // mask families (16-bit fixed-length prefill only; zero / null otherwise)
   int prefix;              // with causal: keys [0, prefix) are seen by every query
   const float* alibi;      // [H] slopes: score += -slope_h * |j - (i + Lk - Lq)|
+  // attention dropout (16-bit fixed-length prefill only; drop_t = 0: none)
+  uint32_t drop_t;         // a key is dropped when its random byte is below drop_t
+  uint32_t seed_lo, seed_hi;
+  float drop_scale;        // 256 / (256 - drop_t)
 };
 
 // Query rows per workgroup and keys per tile of the prefill kernel instance
@@ -92,6 +96,10 @@ struct BwdArgs {
   int nqb;                 // query blocks of bwd_block_rows() rows
   float c;                 // scale * log2(e)
   float scale;
+  // attention dropout of the forward being differentiated (drop_t = 0: none)
+  uint32_t drop_t;
+  uint32_t seed_lo, seed_hi;
+  float drop_scale;        // 256 / (256 - drop_t)
 };
 
 int bwd_block_rows();

@@ -197,6 +197,36 @@ FA355_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const 
                              const int32_t* seqlens_k, void* workspace, size_t workspace_bytes,
                              fa_dtype_t dtype, void* stream);
 
+/*
+ * Attention dropout (training), forward and backward.  The Hugging Face
+ * Flash-Attention-2 integration guide's parameter table lists dropout_p: the
+ * probability of dropping an attention weight, 0 outside training, applied
+ * inside the fused kernel.  Here it acts on the normalised probabilities,
+ * O = (P o Z) V with Z = keep / (1 - p_eff); lse stays that of the undropped
+ * softmax.  Keep decisions: pair (query i, key j) of batch entry b and head
+ * h takes byte (j mod 4), least significant first, of word ((j / 4) mod 4)
+ * of Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with counter
+ * (j / 16, i, h, b) and key (seed mod 2^32, seed / 2^32); the pair is kept
+ * iff that byte is >= t = round(256 * dropout_p), at most 255, so
+ * p_eff = t / 256.  The decisions depend only on (seed, b, h, i, j), so the
+ * backward redraws exactly the forward's.
+ *   dropout_p: in [0, 1) (else FA_ERR_INVALID_ARG); t = 0 is no dropout
+ *   seed: any 64-bit value; use a new one for every forward pass
+ * fa_fwd_dropout: arguments, layout and errors as fa_fwd; fp16/bf16 only
+ * (fp32: FA_ERR_UNSUPPORTED).  fa_bwd_dropout: as fa_bwd, for the o and lse
+ * that fa_fwd_dropout wrote with the same dropout_p and seed.
+ */
+FA355_API fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, int B, int H, int Nq, int Nk, int D, float scale,
+                                     int causal, const int32_t* seqlens_k, float dropout_p,
+                                     uint64_t seed, fa_dtype_t dtype, void* stream);
+FA355_API fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk,
+                                     void* dv, int B, int H, int Nq, int Nk, int D, float scale,
+                                     int causal, const int32_t* seqlens_k, float dropout_p,
+                                     uint64_t seed, void* workspace, size_t workspace_bytes,
+                                     fa_dtype_t dtype, void* stream);
+
 /* Static strings; never NULL. */
 FA355_API const char* fa_status_string(fa_status_t status);
 FA355_API const char* fa_version(void);

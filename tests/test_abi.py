@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
-        "fa_bwd", "fa_bwd_workspace_bytes",
+        "fa_bwd", "fa_bwd_dropout", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
         "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
@@ -212,3 +212,36 @@ def test_bwd_validation():
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(wsb=fa.fa_bwd_workspace_bytes(2, 2, 64) - 1) == fa.FA_ERR_WORKSPACE
     assert call(Nq=0, Nk=0) == fa.FA_OK                          # nothing to do, no device needed
+
+
+def test_dropout_validation():
+    """Argument checks of fa_fwd_dropout and fa_bwd_dropout; all run before any HIP call."""
+    base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=64, Nk=64, D=64, scale=0.1, causal=1,
+                sl=None, p=0.1, seed=7, dtype=fa.FA_BF16, stream=None)
+
+    def fwd(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                 a["Nk"], a["D"], a["scale"], a["causal"], a["sl"], a["p"], a["seed"],
+                                 a["dtype"], a["stream"])
+    assert fwd(p=1.0) == fa.FA_ERR_INVALID_ARG
+    assert fwd(p=-0.01) == fa.FA_ERR_INVALID_ARG
+    assert fwd(p=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert fwd(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED        # 16-bit kernels only
+    assert fwd(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(q=MIS) == fa.FA_ERR_INVALID_ARG
+    assert fwd(Nq=0) == fa.FA_OK
+    assert fwd(Nq=0, seed=(1 << 64) - 1) == fa.FA_OK            # any 64-bit seed
+
+    def bwd(**kw):
+        a = dict(base, do=P, dq=P, dk=P, dv=P, ws=P, wsb=1 << 20)
+        a.update(kw)
+        return fa.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"],
+                                 a["scale"], a["causal"], a["sl"], a["p"], a["seed"], a["ws"],
+                                 a["wsb"], a["dtype"], a["stream"])
+    assert bwd(p=1.5) == fa.FA_ERR_INVALID_ARG
+    assert bwd(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(ws=None) == fa.FA_ERR_WORKSPACE
+    assert bwd(Nq=0, Nk=0) == fa.FA_OK

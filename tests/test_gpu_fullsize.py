@@ -211,3 +211,74 @@ def test_bwd_full_size_heads():
                                           wl.to_f64(do[sl]), w.scale, w.causal)
         for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
             assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref, "%s %s b%d h%d" % (w.name, name, b, h))
+
+
+def test_dropout_full_size_sampled():
+    """The N8192 causal prefill with dropout 0.1, in the launch configuration
+    bench.py --config 10 times: bit-identical reruns, finite outputs, lse
+    equal to the plain call's (dropout leaves the softmax statistics alone),
+    and sampled rows against the oracle with the same keep decisions."""
+    fa = _fa()
+    w = wl.CFG[10]
+    say("generate %s" % w.name)
+    q, k, v = wl.prefill_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    say("fa_fwd_dropout %s" % w.name)
+    o, lse = fa.fwd_dropout(qd, kd, vd, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
+                            scale=w.scale)
+    o2, lse2 = fa.fwd_dropout(qd, kd, vd, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
+                              scale=w.scale)
+    _, lse0 = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse0.view(torch.int32)), "dropout changed lse"
+    assert torch.isfinite(o).all().item()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    t = oracle.drop_threshold(float(np.float32(w.dropout)))
+    ks = oracle.keep_scale(t)
+    rng = np.random.default_rng(1010)
+    for b, h in [(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))]:
+        rows = _sample_rows(rng, w.Nq)
+        kb, vb = wl.to_f64(k[b, :, h]), wl.to_f64(v[b, :, h])
+        keep = oracle.keep_mask(w.seed, b, h, rows, w.Nk, t)
+        o_ref, lse_ref = oracle.attention_rows(wl.to_f64(q[b, rows, h]), rows, kb, vb, w.Nq, w.Nk,
+                                               w.scale, w.causal, keep=keep, keep_scale=ks)
+        assert_close(w.dtype, wl.to_f64(o_c[b, rows, h]) / ks, o_ref / ks,
+                     lse_c[b, h, rows].double().numpy(), lse_ref, "%s b%d h%d" % (w.name, b, h))
+
+
+def test_dropout_bwd_full_size_heads():
+    """Gradients of the N8192 causal prefill with dropout 0.1 (bench.py
+    --config 11): two runs bit-identical, finite, and two whole (batch, head)
+    slices against the oracle's backward with the same keep decisions."""
+    fa = _fa()
+    w = wl.CFG[11]
+    say("generate %s" % w.name)
+    q, k, v = wl.prefill_inputs(w)
+    do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D))
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("fa_fwd_dropout + fa_bwd_dropout %s" % w.name)
+    o, lse = fa.fwd_dropout(qd, kd, vd, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
+                            scale=w.scale)
+    g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dropout_p=w.dropout,
+                seed=w.seed)
+    g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dropout_p=w.dropout,
+                seed=w.seed)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+        assert torch.isfinite(a).all().item()
+    dq, dk, dv = (t.cpu() for t in g1)
+    pf = float(np.float32(w.dropout))
+    for b, h in [(0, 1), (1, 0)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        # the oracle numbers its slices from (0, 0): zero slices in front give
+        # this one its true (b, h) for the keep counters
+        pad = lambda x: np.concatenate([np.zeros((b,) + x.shape[1:]), x], 0) if b else x
+        padh = lambda x: np.concatenate([np.zeros(x.shape[:2] + (h,) + x.shape[3:]), x], 2) if h else x
+        args = [padh(pad(wl.to_f64(t[sl]))) for t in (q, k, v, do)]
+        rq, rk, rv = oracle.attention_bwd(*args, w.scale, w.causal, dropout_p=pf, seed=w.seed)
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref[b:b + 1, :, h:h + 1],
+                              "%s %s b%d h%d" % (w.name, name, b, h))

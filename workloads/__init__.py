@@ -65,6 +65,7 @@ class Workload:
     prefix: int = 0       # prefill with the prefix mask: keys every query sees
     alibi: bool = False   # prefill with ALiBi: slopes of alibi_slopes(H)
     backward: bool = False  # the gradients of the prefill (dQ, dK, dV from dO)
+    dropout: float = 0.0  # attention dropout probability (training), seed = the workload seed
     lens_fixed: Optional[Sequence[int]] = field(default=None, compare=False)
 
     def lengths(self) -> np.ndarray:
@@ -142,6 +143,11 @@ CFG[8] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 ALiBi", alibi=True)
 
 # Beyond the table: the gradients of the N8192 causal prefill.
 CFG[9] = replace(CFG[3], name="backward causal bf16 B4 H16 N8192 D64", backward=True)
+
+# Beyond the table: training-time attention dropout (p = 0.1) in the N8192
+# causal prefill and in its gradients.
+CFG[10] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 dropout 0.1", dropout=0.1)
+CFG[11] = replace(CFG[9], name="backward causal bf16 B4 H16 N8192 D64 dropout 0.1", dropout=0.1)
 
 # Beyond the table: the decode workload over a paged cache (16-row pages at
 # shuffled pool positions), the cache layout of serving runtimes.
