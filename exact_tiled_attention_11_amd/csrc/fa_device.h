@@ -76,6 +76,15 @@ __device__ __forceinline__ float quarter_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Is a wave-wide lane mask (from __builtin_amdgcn_ballot_w64 of a compare)
+// non-zero?  Tested with a scalar compare: the compiler's own lowering of a
+// combined condition round-trips the mask through two vector ops.
+__device__ __forceinline__ bool any_mask(uint64_t m) {
+  uint32_t r;
+  asm volatile("s_cmp_lg_u64 %1, 0\n\ts_cselect_b32 %0, 1, 0" : "=s"(r) : "s"(m) : "scc");
+  return r != 0;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

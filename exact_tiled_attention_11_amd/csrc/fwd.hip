@@ -704,13 +704,18 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     constexpr int r = decltype(rc)::value;
     return *(const frag*)((const char*)smem + kslot(r) + klane[ks]);
   };
+  // lane addresses of the V reads (the LDS base folded in once)
+  FA_LDS(char)* vbase[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    vbase[db] = (FA_LDS(char)*)smem + vlane[db];
+    asm volatile("" : "+v"(vbase[db]));  // kept whole (split, it is re-added every block)
+  }
   auto vfrag = [&](auto rc, int t, int db) __attribute__((always_inline)) -> frag {
     constexpr int r = decltype(rc)::value;
-    const int base = vslot(r) + vlane[db] + 16 * t * RB;
-    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + base));
-    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (FA_LDS(s16x4_t)*)((FA_LDS(char)*)smem + base + 8 * RB));
+    const int off = vslot(r) + 16 * t * RB;
+    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS(s16x4_t)*)(vbase[db] + off));
+    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS(s16x4_t)*)(vbase[db] + off + 8 * RB));
     const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
     const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
     const u32x4_t w = {lo2.x, lo2.y, hi2.x, hi2.y};
@@ -754,8 +759,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // lazy offset: raise m only if a probability could exceed 2^15 or the row
   // has seen no key yet; then rescale O and l and redo the block
   auto settle = [&](float ts) __attribute__((always_inline)) {
-    const bool need = (mrow == -INFINITY) || !(ts <= 0x1p15f);
-    if (__any(need)) {
+    // one ballot per compare, or-ed as scalar masks
+    const uint64_t need = __builtin_amdgcn_ballot_w64(mrow == -INFINITY) |
+                          __builtin_amdgcn_ballot_w64(!(ts <= 0x1p15f));
+    if (any_mask(need)) {
       float m = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, sX[r]);
