@@ -38,6 +38,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = ["exact_tiled_attention_11_amd/csrc/fwd.hip",
                   "exact_tiled_attention_11_amd/csrc/decode.hip",
+                  "exact_tiled_attention_11_amd/csrc/bwd.hip",
                   "exact_tiled_attention_11_amd/csrc/fa_device.h"]
 
 
@@ -56,7 +57,7 @@ def source_hash():
 def counters(name):
     """Per-launch HBM bytes from a committed counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", name)
-    if not os.path.exists(path):
+    if not name or not os.path.exists(path):
         return None
     try:
         with open(path) as f:
@@ -210,10 +211,13 @@ def run_config(n, args, dev):
     else:
         peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
         val, unit, bound = w.flops() / (ms * 1e-3) / 1e12, "TFLOP/s", "mfma"
+    # HBM-side bytes per call from a committed counter summary, where one
+    # exists for this workload and the kernel sources are unchanged since
+    traffic = counters({9: "fa_bwd_causal_bf16_b4h16n8192d64.counters.json"}.get(n, ""))
     print(json.dumps({"config": w.name, "kind": w.kind, "dtype": w.dtype, "value": val, "unit": unit,
                       "ms_per_call": ms, "ms_median": med, "ms_min": t[0], "steps": args.steps,
                       "roofline": {"bound": bound, "achieved": val, "peak": peak, "unit": unit,
-                                   "frac": val / peak}}), flush=True)
+                                   "frac": val / peak, "traffic": traffic}}), flush=True)
 
 
 def main():
