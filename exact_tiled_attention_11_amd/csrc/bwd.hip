@@ -300,15 +300,23 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
       for (int g = 0; g < 4; ++g)
         kw[g] = *(const FA_LDS(uint32_t)*)(trb + col * kTrRow + 8 * g + 4 * hh);
     }
+    // exponents; on a masked chunk a hidden pair's exponent is clamped to
+    // -2^99 or less (probability exactly 0): row cr is visible iff cr >= limv,
+    // tested as min(x, (cr - limv + 1/2) 2^100), exact for |limv| < 2^20
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], a.c, -lr[r]);
+    if (masked) {
+      const int limv = n < lk ? (CAUSAL ? lim : -(1 << 20)) : (1 << 20);
+      const float base = (0.5f - (float)limv) * 0x1p100f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        x[r] = fminf(x[r], base + (float)(8 * (r >> 2) + (r & 3)) * 0x1p100f);
+    }
     float p[16], pd[16], ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = fast_exp2(__builtin_fmaf(s[r], a.c, -lr[r]));
-      if (masked) {
-        const int cr = 8 * (r >> 2) + (r & 3);
-        const bool vis = (n < lk) && (!CAUSAL || cr >= lim);
-        p[r] = vis ? p[r] : 0.f;
-      }
+      p[r] = fast_exp2(x[r]);
       if constexpr (DROP) {
         const bool kp = kept(kw[r >> 2], r & 3, a.drop_t);
         pd[r] = kp ? p[r] : 0.f;
@@ -464,6 +472,17 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     const int lim = last - k0 - 4 * hh;
     uint32_t kw[4];
     if constexpr (DROP) keep_words_rows(kw, k0 >> 4, hh, qi, h, b, a.seed_lo, a.seed_hi);
+    // exponents; on a masked block key offset kr is visible iff kr <= lim,
+    // tested as min(x, (lim - kr + 1/2) 2^100) (hidden: exactly 0 after exp2)
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], a.c, -lrow);
+    if (masked) {
+      const float base = ((float)lim + 0.5f) * 0x1p100f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        x[r] = fminf(x[r], base - (float)(8 * (r >> 2) + (r & 3)) * 0x1p100f);
+    }
     frag dsk[TS];
 #pragma unroll
     for (int t = 0; t < TS; ++t) {
@@ -474,8 +493,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int z = 0; z < 2; ++z) {
           const int r = 8 * t + 2 * e + z;
-          float p = fast_exp2(__builtin_fmaf(s[r], a.c, -lrow));
-          if (masked) p = (8 * (r >> 2) + (r & 3) <= lim) ? p : 0.f;
+          const float p = fast_exp2(x[r]);
           if constexpr (DROP)
             pr[z] = p * ((kept(kw[r >> 2], r & 3, a.drop_t) ? dp[r] * a.drop_scale : 0.f) - drow);
           else
