@@ -1036,8 +1036,14 @@ template <> struct Tile<__bf16, 64> : TileCfg<FA_TILE_16_64> {};
 template <> struct Tile<_Float16, 64> : TileCfg<FA_TILE_16_64> {};
 template <> struct Tile<__bf16, 128> : TileCfg<FA_TILE_16_128> {};
 template <> struct Tile<_Float16, 128> : TileCfg<FA_TILE_16_128> {};
-template <> struct Tile<float, 64> : TileCfg<1, 2, 4, 2, 2> {};
-template <> struct Tile<float, 128> : TileCfg<1, 1, 4, 2, 2> {};
+#ifndef FA_TILE_32_64
+#define FA_TILE_32_64 1, 2, 4, 2, 2
+#endif
+#ifndef FA_TILE_32_128
+#define FA_TILE_32_128 1, 1, 4, 2, 2
+#endif
+template <> struct Tile<float, 64> : TileCfg<FA_TILE_32_64> {};
+template <> struct Tile<float, 128> : TileCfg<FA_TILE_32_128> {};
 
 template <typename K>
 static hipError_t launch_k(K kern, unsigned grid, int threads, int lds, hipStream_t stream,
