@@ -89,6 +89,28 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * CPR + (c ^ swz_f<CPR, F32>(r));
 }
 
+// Row swizzles of the pipelined kernel's K and V slots (16-bit types; CPR =
+// 16-byte chunks per row, 8 for head_dim 64, 16 for 128).  LDS has 64 banks
+// of 4 bytes.  K rows are read by ds_read_b128 (16 lanes, 16 rows, per
+// cycle): the rows of one cycle must fall on distinct 16-byte bank groups.
+// V rows are read by the transposing reads (32 lanes, 4 rows x 4 chunks,
+// per cycle) through one lane offset for rows r, r+8, r+16 and r+24, so the
+// V swizzle depends on bits 0-2 of r only and must separate the 4-chunk
+// groups of the 4 rows.  Both are XOR patterns on the chunk index, hence
+// involutions.  At head_dim 128 the two differ and each read is
+// conflict-free; at head_dim 64 both slots keep the V pattern (its K reads
+// then pair rows r and r+8, a 2-way conflict that measured no slower than a
+// separate K pattern, which costs the dropout instance registers).
+template <int CPR>
+__device__ __forceinline__ int swz_k(int r) {
+  return CPR == 8 ? (((r & 3) << 1) | ((r >> 2) & 1)) : (r & 15);
+}
+template <int CPR>
+__device__ __forceinline__ int swz_v(int r) {
+  return CPR == 8 ? (((r & 3) << 1) | ((r >> 2) & 1))
+                  : (((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r ^ (r >> 2)) & 1) << 3));
+}
+
 // One 16-byte direct-to-LDS load per lane: LDS[m0 + 16*lane] <- buffer[voff].
 // Written as inline assembly because the compiler's own form makes every
 // later LDS read wait for all such loads; this kernel counts them itself.
@@ -617,20 +639,23 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   const char* vp = (const char*)((const T*)a.v + (size_t)wi.k_tok0 * rs + (size_t)wi.h * D);
   const unsigned rsb = (unsigned)(rs * sizeof(T));
 
-  // this lane's 16-byte chunk of a block: row r, LDS position pos
-  unsigned voff[LPS];
+  // this lane's 16-byte chunk of a block: row r, LDS position pos (global
+  // chunk pos ^ swizzle(r))
+  unsigned voffk[LPS], voffv[LPS];
 #pragma unroll
   for (int l = 0; l < LPS; ++l) {
     const int p = (l * NW + wave) * 64 + lane;
     const int r = p / C::kCPR, pos = p % C::kCPR;
-    voff[l] = (unsigned)r * rsb + (unsigned)((pos ^ swz_f<C::kCPR, false>(r)) * 16);
+    voffk[l] = (unsigned)r * rsb + (unsigned)((pos ^ swz_k<C::kCPR>(r)) * 16);
+    voffv[l] = (unsigned)r * rsb + (unsigned)((pos ^ swz_v<C::kCPR>(r)) * 16);
   }
   const unsigned lds0 = (unsigned)(size_t)(FA_LDS(char)*)smem;
   // slot offsets of the block whose index is congruent to r modulo kNS
   constexpr auto kslot = [](int r) { return ((r % C::kNS + C::kNS) % C::kNS) * C::kSlotB; };
   constexpr auto vslot = [](int r) { return C::kVBase + ((r % C::kNS + C::kNS) % C::kNS) * C::kSlotB; };
   // one block of K or V into its slot (an empty range past the last block)
-  auto load = [&](const char* base, int u, int slot) __attribute__((always_inline)) {
+  auto load = [&](const char* base, const unsigned (&voff)[LPS], int u, int slot)
+                  __attribute__((always_inline)) {
     const int rows = (u >= 0 && u < nst) ? min(C::kBC, lk - u * C::kBC) : 0;
     const u32x4_t rsrc = make_rsrc(base + (size_t)(u > 0 ? u : 0) * C::kBC * rsb, (unsigned)rows * rsb);
 #pragma unroll
@@ -640,8 +665,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // step s (s = r mod kNS) requests K of block s+PK+1, then V of block s+PK
   auto issue = [&](int s, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
-    load(kp, s + PK + 1, kslot(r + PK + 1));
-    load(vp, s + PK, vslot(r + PK));
+    load(kp, voffk, s + PK + 1, kslot(r + PK + 1));
+    load(vp, voffv, s + PK, vslot(r + PK));
   };
 
   for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
@@ -669,14 +694,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   int klane[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    klane[ks] = col * RB + ((ks * 2 + hh) ^ swz_f<C::kCPR, false>(col)) * 16;
+    klane[ks] = col * RB + ((ks * 2 + hh) ^ swz_k<C::kCPR>(col)) * 16;
   int vlane[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) {
     const int g = lane >> 4, ii = lane & 15, jj = ii >> 2, qq = ii & 3;
     const int rr = 4 * hh + jj;
     const int ch = 4 * i + 2 * (g & 1) + (qq >> 1);
-    vlane[i] = rr * RB + ((ch ^ swz_f<C::kCPR, false>(rr)) * 16) + (qq & 1) * 8;
+    vlane[i] = rr * RB + ((ch ^ swz_v<C::kCPR>(rr)) * 16) + (qq & 1) * 8;
   }
 
   // nw + 1, hidden from the optimizer: relating it to the loop bound makes
