@@ -144,6 +144,7 @@ fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int Nq, int Nk, int D, float scale, int causal,
                            const int32_t* seqlens_k, float dropout_p, uint64_t seed,
                            fa_dtype_t dtype, void* stream) {
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the dropout kernels are 16-bit only
   uint32_t t = 0;
   float sc = 1.f;
   if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;

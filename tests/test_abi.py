@@ -229,6 +229,7 @@ def test_dropout_validation():
     assert fwd(p=-0.01) == fa.FA_ERR_INVALID_ARG
     assert fwd(p=float("nan")) == fa.FA_ERR_INVALID_ARG
     assert fwd(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED        # 16-bit kernels only
+    assert fwd(dtype=fa.FA_F32, p=0.0) == fa.FA_ERR_UNSUPPORTED
     assert fwd(D=96) == fa.FA_ERR_UNSUPPORTED
     assert fwd(q=MIS) == fa.FA_ERR_INVALID_ARG
     assert fwd(Nq=0) == fa.FA_OK
