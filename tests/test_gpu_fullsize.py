@@ -282,3 +282,40 @@ def test_dropout_bwd_full_size_heads():
         for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
             assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref[b:b + 1, :, h:h + 1],
                               "%s %s b%d h%d" % (w.name, name, b, h))
+
+
+LONG = [
+    # (name, dtype, D, causal, B, H, Nq, Nk): long key loops, a ragged tail, many heads
+    ("causal f16 D128 B1 H2 N65536", "f16", 128, True, 1, 2, 65536, 65536),
+    ("bidirectional bf16 D64 B1 H1 Nq1000 Nk100003", "bf16", 64, False, 1, 1, 1000, 100003),
+    ("causal bf16 D64 B2 H96 N515", "bf16", 64, True, 2, 96, 515, 515),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=lambda c: c[0])
+def test_prefill_long_and_wide_sampled(case):
+    """Sizes beyond the benchmark table: sampled rows against the oracle,
+    every output finite, two runs bit-identical."""
+    name, dtype, D, causal, B, H, Nq, Nk = case
+    fa = _fa()
+    w = wl.Workload(name, "prefill", dtype, H=H, D=D, causal=causal, scale=1 / math.sqrt(D),
+                    seed=77 + Nk, B=B, Nq=Nq, Nk=Nk)
+    say("generate %s" % name)
+    q, k, v = wl.prefill_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    say("fa_fwd %s" % name)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=w.scale)
+    o2, lse2 = fa.fwd(qd, kd, vd, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(2000 + Nk)
+    pairs = sorted({(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))})
+    for b, h in pairs:
+        rows = _sample_rows(rng, Nq, extra=(Nq - 2, 4095, 4096, 32767, 32768))
+        o_ref, lse_ref = oracle.attention_rows(wl.to_f64(q[b, rows, h]), rows, wl.to_f64(k[b, :, h]),
+                                               wl.to_f64(v[b, :, h]), Nq, Nk, w.scale, causal)
+        assert_close(dtype, wl.to_f64(o_c[b, rows, h]), o_ref, lse_c[b, h, rows].double().numpy(),
+                     lse_ref, "%s b%d h%d" % (name, b, h))
