@@ -319,3 +319,49 @@ def test_prefill_long_and_wide_sampled(case):
                                                wl.to_f64(v[b, :, h]), Nq, Nk, w.scale, causal)
         assert_close(dtype, wl.to_f64(o_c[b, rows, h]), o_ref, lse_c[b, h, rows].double().numpy(),
                      lse_ref, "%s b%d h%d" % (name, b, h))
+
+
+@pytest.mark.parametrize("chunk", [128, 512])
+def test_decode_long_cache_sampled(chunk):
+    """Decode against caches of 131072 and 100001 keys (1024 / 256 chunks):
+    contiguous and paged calls bit-identical, sampled heads against the oracle."""
+    fa = _fa()
+    B, H, D, Nk = 2, 8, 128, 131072
+    lens = np.array([131072, 100001], dtype=np.int64)
+    w = wl.Workload("decode long", "decode", "bf16", H=H, D=D, causal=False, scale=1 / math.sqrt(D),
+                    seed=91, B=B, Nk=Nk, len_lo=1, len_hi=Nk, chunk=chunk, lens_fixed=list(lens))
+    q = wl.decode_query(w)
+    kc = torch.zeros((B, Nk, H, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for b in range(B):
+        L = int(lens[b])
+        kc[b, :L].copy_(wl.decode_cache_rows(w, 1, b, L))
+        vc[b, :L].copy_(wl.decode_cache_rows(w, 2, b, L))
+        if L < Nk:
+            kc[b, L:] = float("nan")
+            vc[b, L:] = float("nan")
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    say("fa_decode_splitkv Lk %s chunk %d" % (lens.tolist(), chunk))
+    o, lse = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=chunk)
+    ps = 64
+    table = torch.arange(B * (Nk // ps), dtype=torch.int32, device="cuda").view(B, Nk // ps)
+    table = table.flip(1).contiguous()  # pages in reverse pool order
+    kp = torch.empty((B * Nk // ps, ps, H, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[table.flatten().long()] = kc.view(-1, ps, H, D)
+    vp[table.flatten().long()] = vc.view(-1, ps, H, D)
+    op, lp = fa.decode_splitkv_paged(q.cuda(), kp, vp, sl, table, scale=w.scale, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), op.view(torch.int16)), "paged differs from contiguous"
+    assert torch.equal(lse.view(torch.int32), lp.view(torch.int32))
+    o_c, lse_c = o.cpu(), lse.cpu()
+    del kc, vc, kp, vp
+    for b in range(B):
+        L = int(lens[b])
+        kb = wl.to_f64(wl.decode_cache_rows(w, 1, b, L))
+        vb = wl.to_f64(wl.decode_cache_rows(w, 2, b, L))
+        for h in (0, H - 1):
+            o_ref, lse_ref = oracle.attention_rows(wl.to_f64(q[b, h])[None], [0], kb[:, h], vb[:, h], 1,
+                                                   L, w.scale, False)
+            assert_close("bf16", wl.to_f64(o_c[b, h])[None], o_ref, lse_c[b, h:h + 1].double().numpy(),
+                         lse_ref, "decode Lk%d chunk%d h%d" % (L, chunk, h))
