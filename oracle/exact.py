@@ -192,7 +192,8 @@ def attention_dropout(q, k, v, scale, causal, dropout_p, seed, seqlens_k=None, r
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, seed=0):
+def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, seed=0, prefix=0,
+                  alibi_slopes=None):
     """Gradients of the forward definition: given dO = dL/dO, returns
     (dQ, dK, dV) in the BSHD layout, float64.
 
@@ -208,6 +209,9 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, see
     With dropout (``oracle.dropout``), O = (P o Z) V with Z = keep * scale;
     then dV = (P o Z)ᵀ dO, dP = (dO Vᵀ) o Z, and the rest is unchanged
     (rowsum(dO o O) still equals rowsum(P o dP)).
+    ``prefix`` and ``alibi_slopes`` select the forward's prefix mask and
+    ALiBi bias (``visible``, ``alibi_bias``): the bias does not depend on q or
+    k, so it changes P but not the form of dS.
     """
     q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
     B, nq, H, D = q.shape
@@ -225,7 +229,9 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, see
             vv = np.asarray(v[b, :lk, h], _F64)
             g = np.asarray(do[b, :, h], _F64)
             s = scores(qq, kk, scale)
-            vis = visible(np.arange(nq), nq, lk, causal)
+            if alibi_slopes is not None:
+                s = s + alibi_bias(np.arange(nq), nq, lk, alibi_slopes[h])
+            vis = visible(np.arange(nq), nq, lk, causal, prefix)
             s = np.where(vis, s, -np.inf)
             m = s.max(axis=1)
             m_shift = np.where(np.isneginf(m), 0.0, m)

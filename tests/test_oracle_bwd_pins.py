@@ -155,3 +155,90 @@ def test_planted_bwd_mistakes_are_caught(kind):
         except AssertionError:
             caught += 1
     assert caught > 0, "no pin caught the planted mistake: %s" % kind
+
+
+# ----------------------------------------------------------------------------
+# Prefix mask and ALiBi bias (the forward's mask families)
+# ----------------------------------------------------------------------------
+
+MASK_CASES = [
+    # (B, nq, nk, H, D, causal, prefix, alibi)
+    (1, 7, 9, 2, 4, True, 3, False),
+    (2, 6, 6, 2, 3, True, 0, True),
+    (1, 5, 8, 2, 4, False, 0, True),
+    (1, 8, 8, 3, 4, True, 4, True),
+]
+
+
+def _masked_case(case, seed):
+    B, nq, nk, H, D, causal, prefix, alibi = case
+    rng = np.random.default_rng(seed)
+    q, k, v, do = rnd(rng, B, nq, H, D), rnd(rng, B, nk, H, D), rnd(rng, B, nk, H, D), rnd(rng, B, nq, H, D)
+    slopes = 2.0 ** (-8.0 * (np.arange(H) + 1) / H) * 3.0 if alibi else None
+    return q, k, v, do, causal, prefix, slopes
+
+
+def _masked_fd(bwd, case, seed, eps=1e-6):
+    q, k, v, do, causal, prefix, slopes = _masked_case(case, seed)
+    scale = 0.45
+    got = bwd(q, k, v, do, scale, causal, prefix, slopes)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, scale, causal, prefix=prefix, alibi_slopes=slopes)
+        return float((o * do).sum())
+    rng = np.random.default_rng(seed + 1)
+    for which, g in enumerate(got):
+        args = [q, k, v]
+        x = args[which]
+        for _ in range(10):
+            ix = tuple(rng.integers(0, s) for s in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[ix] += eps
+            xm[ix] -= eps
+            ap, am = list(args), list(args)
+            ap[which], am[which] = xp, xm
+            num = (loss(*ap) - loss(*am)) / (2 * eps)
+            assert abs(num - g[ix]) < 2e-7 + 1e-6 * abs(num), (which, ix, num, g[ix])
+
+
+def _oracle_masked_bwd(q, k, v, do, scale, causal, prefix, slopes):
+    return oracle.attention_bwd(q, k, v, do, scale, causal, prefix=prefix, alibi_slopes=slopes)
+
+
+@pytest.mark.parametrize("i", range(len(MASK_CASES)))
+def test_masked_bwd_matches_finite_differences(i):
+    _masked_fd(_oracle_masked_bwd, MASK_CASES[i], 300 + i)
+
+
+@pytest.mark.parametrize("i", range(len(MASK_CASES)))
+def test_masked_bwd_matches_torch_cpu_float64_autograd(i):
+    q, k, v, do, causal, prefix, slopes = _masked_case(MASK_CASES[i], 400 + i)
+    B, nq, H, D = q.shape
+    nk = k.shape[1]
+    scale = 0.45
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * torch.einsum("bihd,bjhd->bhij", tq, tk)
+    ii = torch.arange(nq)[:, None]
+    jj = torch.arange(nk)[None, :]
+    if slopes is not None:
+        dist = (jj - (ii + nk - nq)).abs().to(torch.float64)
+        s = s - torch.tensor(slopes)[None, :, None, None] * dist
+    if causal:
+        vis = (jj <= ii + nk - nq) | (jj < prefix)
+        s = s.masked_fill(~vis, float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), tv)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    got = oracle.attention_bwd(q, k, v, do, scale, causal, prefix=prefix, alibi_slopes=slopes)
+    for g, t in zip(got, (tq, tk, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["bias dropped", "prefix ignored"])
+def test_planted_masked_bwd_mistakes_are_caught(kind):
+    def bad(q, k, v, do, scale, causal, prefix, slopes):
+        if kind == "bias dropped":
+            return oracle.attention_bwd(q, k, v, do, scale, causal, prefix=prefix)
+        return oracle.attention_bwd(q, k, v, do, scale, causal, alibi_slopes=slopes)
+    case = MASK_CASES[3]
+    with pytest.raises(AssertionError):
+        _masked_fd(bad, case, 303)
