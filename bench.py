@@ -136,15 +136,20 @@ def run_config(n, args, dev):
     if w.kind == "prefill" and w.backward:
         q, k, v = make_prefill(w, dev)
         do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D)).to(dev)
+        sd = torch.from_numpy(wl.alibi_slopes(w.H)).to(dev) if w.alibi else None
         if w.dropout:
             o, lse = fa.fwd_dropout(q, k, v, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
                                     scale=w.scale)
+        elif w.prefix or w.alibi:
+            o, lse = fa.fwd_masked(q, k, v, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                                   alibi_slopes=sd)
         else:
             o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.Nq), dtype=torch.uint8, device=dev)
         call = lambda: fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
-                              dv=dv, dropout_p=w.dropout, seed=w.seed, workspace=ws)
+                              dv=dv, dropout_p=w.dropout, seed=w.seed, prefix=w.prefix,
+                              alibi_slopes=sd, workspace=ws)
     elif w.kind == "prefill":
         q, k, v = make_prefill(w, dev)
         o = torch.empty_like(q)
@@ -230,13 +235,14 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
-    ap.add_argument("--config", type=int, choices=list(range(1, 12)), default=None,
+    ap.add_argument("--config", type=int, choices=list(range(1, 14)), default=None,
                     help="time one workload alone (its library call only) and print a JSON "
                          "line for it instead of the bench line: 1-5 the benchmark table, "
                          "6 its decode over a paged cache, 7 / 8 its N8192 causal prefill "
                          "with a 2048-key prefix mask / with ALiBi, 9 the gradients of "
                          "that prefill (fa_bwd), 10 / 11 that prefill / its gradients with "
-                         "attention dropout 0.1")
+                         "attention dropout 0.1, 12 / 13 the gradients with the prefix mask / "
+                         "with ALiBi")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "

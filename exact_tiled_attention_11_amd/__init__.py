@@ -26,7 +26,7 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
-    "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout",
+    "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_masked", "fa_bwd_dropout",
     "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
     "fwd", "fwd_masked", "fwd_dropout", "bwd", "fwd_varlen", "decode_splitkv",
@@ -49,6 +49,8 @@ _SIGS = {
                             _i, _vp]),
     "fa_bwd_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                             _i, _vp, _f, _u64, _vp, _sz, _i, _vp]),
+    "fa_bwd_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                           _i, _vp, _i, _vp, _vp, _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _vp, _sz, _i, _vp]),
@@ -119,6 +121,13 @@ def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, ca
     return load().fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal,
                                  seqlens_k, dropout_p, seed, workspace, workspace_bytes, dtype,
                                  stream)
+
+
+def fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k,
+                  prefix, alibi_slopes, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal,
+                                seqlens_k, prefix, alibi_slopes, workspace, workspace_bytes, dtype,
+                                stream)
 
 
 def fa_bwd_workspace_bytes(B, H, Nq) -> int:
@@ -275,10 +284,11 @@ def fwd_dropout(q, k, v, *, dropout_p: float, seed: int, causal: bool = False,
 
 
 def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
-        seqlens_k=None, dropout_p: float = 0.0, seed: int = 0, dq=None, dk=None, dv=None,
-        workspace=None, stream=None) -> Tuple:
+        seqlens_k=None, dropout_p: float = 0.0, seed: int = 0, prefix: int = 0,
+        alibi_slopes=None, dq=None, dk=None, dv=None, workspace=None, stream=None) -> Tuple:
     """Gradients (dq, dk, dv) for the forward fwd(q, k, v) that produced o and lse, given dout
-    (with dropout_p > 0: for fwd_dropout with the same dropout_p and seed)."""
+    (with dropout_p > 0: for fwd_dropout with the same dropout_p and seed; with prefix or
+    alibi_slopes: for fwd_masked with the same ones)."""
     import torch
     B, Nq, H, D = q.shape
     Nk = k.shape[1]
@@ -290,6 +300,18 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] =
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
                                 device=q.device)
+    if dropout_p and (prefix or alibi_slopes is not None):
+        raise ValueError("dropout with the prefix mask or ALiBi has no backward")
+    if prefix or alibi_slopes is not None:
+        if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
+                                         alibi_slopes.numel() != H):
+            raise ValueError("alibi_slopes must be float32[H]")
+        st = fa_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                           _ptr(seqlens_k), int(prefix), _ptr(alibi_slopes), _ptr(workspace),
+                           workspace.numel(), _dtype_code(q), _stream(stream))
+        _check("fa_bwd_masked", st)
+        return dq, dk, dv
     if dropout_p:
         st = fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                             _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)),

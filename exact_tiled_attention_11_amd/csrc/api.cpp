@@ -111,9 +111,9 @@ fa_status_t fwd_fixed(const void* q, const void* k, const void* v, void* o, floa
 
 fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
-                     int D, float scale, int causal, const int32_t* seqlens_k, uint32_t drop_t,
-                     float drop_scale, uint64_t seed, void* workspace, size_t workspace_bytes,
-                     fa_dtype_t dtype, void* stream);
+                     int D, float scale, int causal, const int32_t* seqlens_k, int prefix,
+                     const float* alibi_slopes, uint32_t drop_t, float drop_scale, uint64_t seed,
+                     void* workspace, size_t workspace_bytes, fa_dtype_t dtype, void* stream);
 
 }  // namespace
 
@@ -169,8 +169,18 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                    int D, float scale, int causal, const int32_t* seqlens_k, void* workspace,
                    size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
-  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, 0u,
-                  1.f, 0u, workspace, workspace_bytes, dtype, stream);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, 0,
+                  nullptr, 0u, 1.f, 0u, workspace, workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                          int H, int Nq, int Nk, int D, float scale, int causal,
+                          const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
+                          void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                          void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k,
+                  prefix, alibi_slopes, 0u, 1.f, 0u, workspace, workspace_bytes, dtype, stream);
 }
 
 fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
@@ -182,8 +192,8 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const vo
   uint32_t t = 0;
   float sc = 1.f;
   if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
-  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, t,
-                  sc, seed, workspace, workspace_bytes, dtype, stream);
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, 0,
+                  nullptr, t, sc, seed, workspace, workspace_bytes, dtype, stream);
 }
 
 }  // extern "C"
@@ -192,14 +202,16 @@ namespace {
 
 fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
-                     int D, float scale, int causal, const int32_t* seqlens_k, uint32_t drop_t,
-                     float drop_scale, uint64_t seed, void* workspace, size_t workspace_bytes,
-                     fa_dtype_t dtype, void* stream) {
+                     int D, float scale, int causal, const int32_t* seqlens_k, int prefix,
+                     const float* alibi_slopes, uint32_t drop_t, float drop_scale, uint64_t seed,
+                     void* workspace, size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit only
   if (B < 1 || H < 1 || Nq < 0 || Nk < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (prefix < 0 || (prefix > 0 && !causal)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)alibi_slopes & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (Nq == 0 && Nk == 0) return FA_OK;
   if ((Nq > 0 && (!q || !o || !lse || !dout || !dq)) || (Nk > 0 && (!k || !v || !dk || !dv)))
     return FA_ERR_INVALID_ARG;
@@ -242,6 +254,8 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
   a.seed_lo = (uint32_t)seed;
   a.seed_hi = (uint32_t)(seed >> 32);
   a.drop_scale = drop_scale;
+  a.prefix = prefix;
+  a.alibi = alibi_slopes;
   return from_hip(fa::launch_bwd(a, dtype, D, causal != 0, (hipStream_t)stream));
 }
 

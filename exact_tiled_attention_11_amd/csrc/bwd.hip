@@ -43,6 +43,10 @@ namespace fa {
 namespace {
 
 constexpr int kNW = 4;     // waves per workgroup
+
+// MODE of the gradient kernels: plain, with the ALiBi bias of the forward,
+// or with its attention dropout (the prefix mask is a runtime value in all)
+constexpr int kBwdPlain = 0, kBwdAlibi = 1, kBwdDrop = 2;
 constexpr int kRows = 32;  // rows per wave and per streamed tile
 
 // LDS position (16-byte chunks) of chunk c of tile row r: the XOR pattern of
@@ -174,8 +178,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 constexpr int kTrRow = 36;
 constexpr int kTrWave = 32 * kTrRow;
 
-template <typename T, int D, bool CAUSAL, bool DROP>
+template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
   using E = Elem<T>;
   using frag = typename E::frag;
   using TP = TilePair<T, D>;
@@ -226,11 +231,14 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 
   // query chunks that see any key of the workgroup (causal: i >= k0 - off)
   const int nch = (lq + kRows - 1) / kRows;
+  // (with a prefix mask, keys below it are seen by every row)
   int c_begin = 0, c_wave = 0;
   if (CAUSAL) {
-    c_begin = max(0, k0 - off) / kRows;
-    c_wave = max(0, kw0 - off) / kRows;
+    c_begin = k0 < a.prefix ? 0 : max(0, k0 - off) / kRows;
+    c_wave = kw0 < a.prefix ? 0 : max(0, kw0 - off) / kRows;
   }
+  const int pre = a.prefix - 1;  // keys 0 .. pre are visible to every causal row
+  const float slope2 = ALIBI ? a.alibi[h] * kLog2e : 0.f;  // ALiBi slope in exp2 units
   const bool wave_live = kw0 < lk;
 
   ReadLanes<D> rl;
@@ -283,8 +291,10 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
         dr[4 * g + e] = d4[e];
       }
     }
-    const bool masked = (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > q0 + off);
-    // query row m of the chunk sees this lane's key iff m >= lim (and the key is real)
+    const bool masked =
+        (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > max(q0 + off, pre));
+    // query row m of the chunk sees this lane's key iff m >= lim (and the key is
+    // real); the key's distance to that row's own position is lim - m
     const int lim = n - q0 - off - 4 * hh;
     uint32_t kw[4];
     if constexpr (DROP) {
@@ -306,8 +316,15 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], a.c, -lr[r]);
+    if constexpr (ALIBI) {  // - slope |key - (row + Lk - Lq)|
+      const float fl = (float)lim;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        x[r] = __builtin_fmaf(-slope2, fabsf(fl - (float)(8 * (r >> 2) + (r & 3))), x[r]);
+    }
     if (masked) {
-      const int limv = n < lk ? (CAUSAL ? lim : -(1 << 20)) : (1 << 20);
+      const int limv =
+          n < lk ? (CAUSAL && n >= a.prefix ? lim : -(1 << 20)) : (1 << 20);
       const float base = (0.5f - (float)limv) * 0x1p100f;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -388,8 +405,11 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 // ---------------------------------------------------------------------------
 // dQ: a workgroup per 128 query rows of one (batch, head)
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
+// (four waves per SIMD fit the causal head_dim-64 instance without spills,
+// measured 1 % faster; the others keep the compiler's choice)
+template <typename T, int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
   using E = Elem<T>;
   using frag = typename E::frag;
   using TP = TilePair<T, D>;
@@ -442,11 +462,14 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16_t{};
 
   // key blocks of the workgroup and of this wave (causal: keys <= row + off)
+  // (row i sees keys 0 .. max(i + off, prefix - 1) under the causal mask)
+  const int pre = a.prefix - 1;
+  const float slope2 = ALIBI ? a.alibi[h] * kLog2e : 0.f;  // ALiBi slope in exp2 units
   int nkb = (lk + kRows - 1) / kRows, nkw = nkb;
   if (CAUSAL) {
-    const int kmax = min(q0 + kNW * kRows, lq) - 1 + off;
+    const int kmax = max(min(q0 + kNW * kRows, lq) - 1 + off, pre);
     nkb = kmax < 0 ? 0 : min(nkb, kmax / kRows + 1);
-    const int t = wq_last + off;
+    const int t = max(wq_last + off, pre);
     nkw = (wq_last < wq0 || t < 0) ? 0 : min(nkb, t / kRows + 1);
   } else if (wq_last < wq0) {
     nkw = 0;
@@ -466,9 +489,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
       s = mma(row_frag<frag>(tk, rl.rowl[ks]), qf[ks], s);
       dp = mma(row_frag<frag>(tv, rl.rowl[ks]), dof[ks], dp);
     }
-    const bool masked = (k0 + kRows > lk) || (CAUSAL && k0 + kRows - 1 > wq0 + off);
+    const bool masked = (k0 + kRows > lk) || (CAUSAL && k0 + kRows - 1 > max(wq0 + off, pre));
     // key 8*(r>>2) + 4*hh + (r&3) of the block is visible iff that offset <= lim
-    const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;
+    const int last = CAUSAL ? min(max(qi + off, pre), lk - 1) : lk - 1;
     const int lim = last - k0 - 4 * hh;
     uint32_t kw[4];
     if constexpr (DROP) keep_words_rows(kw, k0 >> 4, hh, qi, h, b, a.seed_lo, a.seed_hi);
@@ -477,6 +500,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(BwdArgs a) {
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], a.c, -lrow);
+    if constexpr (ALIBI) {  // - slope |key - (qi + Lk - Lq)|, key k0 + 4hh + offset
+      const float d0 = (float)(k0 + 4 * hh - qi - off);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        x[r] = __builtin_fmaf(-slope2, fabsf(d0 + (float)(8 * (r >> 2) + (r & 3))), x[r]);
+    }
     if (masked) {
       const float base = ((float)lim + 0.5f) * 0x1p100f;
 #pragma unroll
@@ -558,27 +587,24 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
   const unsigned nbh = (unsigned)(a.B * a.H);
   const unsigned gk = (unsigned)((a.Nk + kNW * kRows - 1) / (kNW * kRows)) * nbh;
   const unsigned gq = (unsigned)a.nqb * nbh;
-  const bool drop = a.drop_t != 0;
-  if (gk > 0) {
-    if (drop) {
-      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), dim3(gk), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), dim3(gk), dim3(kNW * 64), 0, stream, a);
-    } else {
-      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), dim3(gk), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+  const int mode = a.drop_t ? kBwdDrop : (a.alibi ? kBwdAlibi : kBwdPlain);
+  auto launch2 = [&](auto mc) {
+    constexpr int M = decltype(mc)::value;
+    if (gk > 0) {
+      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, M>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, M>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      const hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return e2;
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (gq > 0) {
-    if (drop) {
-      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true>), dim3(gq), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true>), dim3(gq), dim3(kNW * 64), 0, stream, a);
-    } else {
-      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false>), dim3(gq), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+    if (gq > 0) {
+      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, M>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, M>), dim3(gq), dim3(kNW * 64), 0, stream, a);
     }
-  }
-  return hipGetLastError();
+    return hipGetLastError();
+  };
+  if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{});
+  if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{});
+  return launch2(std::integral_constant<int, kBwdPlain>{});
 }
 
 int bwd_block_rows() { return kNW * kRows; }

@@ -100,6 +100,9 @@ struct BwdArgs {
   uint32_t drop_t;
   uint32_t seed_lo, seed_hi;
   float drop_scale;        // 256 / (256 - drop_t)
+  // mask families of the forward being differentiated (zero / null: none)
+  int prefix;              // with causal: keys [0, prefix) are seen by every query
+  const float* alibi;      // [H] slopes: score += -slope_h * |j - (i + Lk - Lq)|
 };
 
 int bwd_block_rows();

@@ -198,6 +198,23 @@ FA355_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const 
                              fa_dtype_t dtype, void* stream);
 
 /*
+ * Backward pass of fa_fwd_masked: as fa_bwd, for the o and lse that
+ * fa_fwd_masked wrote with the same prefix and alibi_slopes (prefix mask:
+ * with causal only, keys [0, prefix) are seen by every query; ALiBi: score
+ * += -slope_h * |j - (i + Lk - Lq)|).  The bias does not depend on q or k,
+ * so it changes the recomputed probabilities only.
+ *   prefix: >= 0, and 0 unless causal (else FA_ERR_INVALID_ARG)
+ *   alibi_slopes: NULL or a 4-byte aligned device array of H floats
+ * Other arguments, layouts, errors and ordering as fa_bwd.
+ */
+FA355_API fa_status_t fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk,
+                                    void* dv, int B, int H, int Nq, int Nk, int D, float scale,
+                                    int causal, const int32_t* seqlens_k, int prefix,
+                                    const float* alibi_slopes, void* workspace,
+                                    size_t workspace_bytes, fa_dtype_t dtype, void* stream);
+
+/*
  * Attention dropout (training), forward and backward.  The Hugging Face
  * Flash-Attention-2 integration guide's parameter table lists dropout_p: the
  * probability of dropping an attention weight, 0 outside training, applied

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
-        "fa_bwd", "fa_bwd_dropout", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
+        "fa_bwd", "fa_bwd_dropout", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
         "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
@@ -246,3 +246,23 @@ def test_dropout_validation():
     assert bwd(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
     assert bwd(ws=None) == fa.FA_ERR_WORKSPACE
     assert bwd(Nq=0, Nk=0) == fa.FA_OK
+
+
+def test_bwd_masked_validation():
+    base = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, Nq=64, Nk=64, D=64,
+                scale=0.1, causal=1, sl=None, prefix=8, alibi=P, ws=P, wsb=1 << 20,
+                dtype=fa.FA_BF16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                                a["causal"], a["sl"], a["prefix"], a["alibi"], a["ws"], a["wsb"],
+                                a["dtype"], a["stream"])
+    assert call(prefix=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(causal=0) == fa.FA_ERR_INVALID_ARG              # a prefix needs the causal mask
+    assert call(alibi=P + 2) == fa.FA_ERR_INVALID_ARG           # float slopes not 4-byte aligned
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(Nq=0, Nk=0) == fa.FA_OK

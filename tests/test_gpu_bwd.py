@@ -96,3 +96,62 @@ BWD = [
 @pytest.mark.parametrize("w,seqlens", BWD, ids=lambda x: getattr(x, "name", str(x)))
 def test_bwd(w, seqlens):
     bwd_case(w, seqlens)
+
+
+def masked_bwd_case(w, prefix, alibi, seqlens=None):
+    """fa_fwd_masked then fa_bwd_masked against the oracle's masked backward."""
+    import exact_tiled_attention_11_amd as fa
+    fa.load()
+    q, k, v = wl.prefill_inputs(w)
+    do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D))
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            k[b, L:] = float("nan")
+            v[b, L:] = float("nan")
+    slopes = wl.alibi_slopes(w.H) if alibi else None
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("  fa_fwd_masked + fa_bwd_masked %s prefix %d alibi %s" % (w.name, prefix, alibi))
+    o, lse = fa.fwd_masked(qd, kd, vd, causal=w.causal, scale=w.scale, seqlens_k=sl, prefix=prefix,
+                           alibi_slopes=sd)
+    outs = []
+    for rep in range(2):
+        dq = torch.full_like(qd, float("nan"))
+        dk = torch.full_like(kd, float("nan"))
+        dv = torch.full_like(vd, float("nan"))
+        fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, seqlens_k=sl, prefix=prefix,
+               alibi_slopes=sd, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+    dq, dk, dv = outs[0]
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            assert (dk[b, L:] == 0).all() and (dv[b, L:] == 0).all(), "padding keys get no gradient"
+    rq, rk, rv = oracle.attention_bwd(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), wl.to_f64(do),
+                                      w.scale, w.causal, seqlens_k=seqlens, prefix=prefix,
+                                      alibi_slopes=slopes)
+    tag = "%s prefix %d alibi %s" % (w.name, prefix, alibi)
+    assert_grad_close(w.dtype, wl.to_f64(dq), rq, "%s dq" % tag)
+    assert_grad_close(w.dtype, wl.to_f64(dk), rk, "%s dk" % tag)
+    assert_grad_close(w.dtype, wl.to_f64(dv), rv, "%s dv" % tag)
+
+
+MASKED_BWD = [
+    (P("bf16 D64 causal B2 H3 N300", "bf16", 64, True, 2, 3, 300, 300, 61), 37, False, None),
+    (P("bf16 D64 causal Nq100 Nk300", "bf16", 64, True, 1, 2, 100, 300, 62), 150, False, None),
+    (P("bf16 D64 causal Nq300 Nk100", "bf16", 64, True, 1, 2, 300, 100, 63), 20, False, None),
+    (P("bf16 D64 causal B2 H4 N300 ALiBi", "bf16", 64, True, 2, 4, 300, 300, 64), 0, True, None),
+    (P("bf16 D64 bidirectional Nq129 Nk200 ALiBi", "bf16", 64, False, 1, 4, 129, 200, 65), 0, True, None),
+    (P("f16 D128 causal N257 prefix+ALiBi", "f16", 128, True, 1, 2, 257, 257, 66), 64, True, None),
+    (P("f16 D64 causal B2 H2 N300 padded, prefix", "f16", 64, True, 2, 2, 300, 300, 67), 200,
+     False, [300, 177]),
+]
+
+
+@pytest.mark.parametrize("w,prefix,alibi,seqlens", MASKED_BWD,
+                         ids=lambda x: getattr(x, "name", str(x)))
+def test_bwd_masked(w, prefix, alibi, seqlens):
+    masked_bwd_case(w, prefix, alibi, seqlens)

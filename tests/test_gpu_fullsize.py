@@ -365,3 +365,37 @@ def test_decode_long_cache_sampled(chunk):
                                                    L, w.scale, False)
             assert_close("bf16", wl.to_f64(o_c[b, h])[None], o_ref, lse_c[b, h:h + 1].double().numpy(),
                          lse_ref, "decode Lk%d chunk%d h%d" % (L, chunk, h))
+
+
+@pytest.mark.parametrize("cfg", [12, 13])
+def test_bwd_masked_full_size_heads(cfg):
+    """Gradients of the N8192 causal prefill with the 2048-key prefix mask /
+    with ALiBi (bench.py --config 12 / 13): reruns bit-identical, finite, and
+    two whole (batch, head) slices against the oracle's masked backward."""
+    fa = _fa()
+    w = wl.CFG[cfg]
+    say("generate %s" % w.name)
+    q, k, v = wl.prefill_inputs(w)
+    do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D))
+    slopes = wl.alibi_slopes(w.H) if w.alibi else None
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("fa_fwd_masked + fa_bwd_masked %s" % w.name)
+    o, lse = fa.fwd_masked(qd, kd, vd, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                           alibi_slopes=sd)
+    g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                alibi_slopes=sd)
+    g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                alibi_slopes=sd)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+        assert torch.isfinite(a).all().item()
+    dq, dk, dv = (t.cpu() for t in g1)
+    for b, h in [(0, 0), (w.B - 1, w.H - 1)]:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        rq, rk, rv = oracle.attention_bwd(wl.to_f64(q[sl]), wl.to_f64(k[sl]), wl.to_f64(v[sl]),
+                                          wl.to_f64(do[sl]), w.scale, w.causal, prefix=w.prefix,
+                                          alibi_slopes=None if slopes is None else slopes[h:h + 1])
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref, "%s %s b%d h%d" % (w.name, name, b, h))
