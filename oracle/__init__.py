@@ -20,6 +20,7 @@ from .exact import (  # noqa: F401
     attention_dropout,
     attention_bwd,
     attention_varlen,
+    attention_varlen_bwd,
     decode,
     decode_paged,
     partial,

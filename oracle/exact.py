@@ -43,11 +43,15 @@ from . import dropout as _dropout
 __all__ = [
     "scores",
     "visible",
+    "alibi_bias",
     "attention_rows",
     "attention",
     "attention_dropout",
+    "attention_bwd",
     "attention_varlen",
+    "attention_varlen_bwd",
     "decode",
+    "decode_paged",
     "partial",
     "merge",
     "finalize",
@@ -279,6 +283,25 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, row_chu
                 o[q0 + r0:q0 + r1, h, :] = ob
                 lse[h, q0 + r0:q0 + r1] = lb
     return o, lse
+
+
+def attention_varlen_bwd(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale, causal):
+    """Gradients of ``attention_varlen``: each packed sequence is its own
+    attention problem, so its rows of (dQ, dK, dV) are ``attention_bwd`` of
+    that sequence alone.  q, do: [total_q, H, D]; k, v: [total_k, H, D].
+    Keys outside every sequence get zero gradients.
+    """
+    q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
+    dq = np.zeros(q.shape, _F64)
+    dk = np.zeros(k.shape, _F64)
+    dv = np.zeros(v.shape, _F64)
+    for s in range(len(cu_seqlens_q) - 1):
+        q0, q1 = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
+        k0, k1 = int(cu_seqlens_k[s]), int(cu_seqlens_k[s + 1])
+        gq, gk, gv = attention_bwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], do[None, q0:q1],
+                                   scale, causal)
+        dq[q0:q1], dk[k0:k1], dv[k0:k1] = gq[0], gk[0], gv[0]
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, seqlens_k, scale):

@@ -242,3 +242,48 @@ def test_planted_masked_bwd_mistakes_are_caught(kind):
     case = MASK_CASES[3]
     with pytest.raises(AssertionError):
         _masked_fd(bad, case, 303)
+
+
+# ----------------------------------------------------------------------------
+# Packed variable-length batches
+# ----------------------------------------------------------------------------
+
+def _varlen_fd(bwd, causal, seed, eps=1e-6):
+    rng = np.random.default_rng(seed)
+    cu_q = np.array([0, 3, 3, 8, 12])   # an empty sequence included
+    cu_k = np.array([0, 4, 6, 11, 13])
+    H, D, scale = 2, 3, 0.6
+    q, do = rnd(rng, 12, H, D), rnd(rng, 12, H, D)
+    k, v = rnd(rng, 13, H, D), rnd(rng, 13, H, D)
+    got = bwd(q, k, v, do, cu_q, cu_k, scale, causal)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention_varlen(qq, kk, vv, cu_q, cu_k, scale, causal)
+        return float((o * do).sum())
+    for which, g in enumerate(got):
+        args = [q, k, v]
+        x = args[which]
+        for ix in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[ix] += eps
+            xm[ix] -= eps
+            ap, am = list(args), list(args)
+            ap[which], am[which] = xp, xm
+            num = (loss(*ap) - loss(*am)) / (2 * eps)
+            assert abs(num - g[ix]) < 2e-7 + 1e-6 * abs(num), (which, ix, num, g[ix])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_bwd_matches_finite_differences(causal):
+    """Every entry of the gradients against central differences through the
+    (separately pinned) packed forward; keys of the empty query sequence get 0."""
+    _varlen_fd(oracle.attention_varlen_bwd, causal, 500 + causal)
+
+
+def test_planted_varlen_bwd_mistake_is_caught():
+    """Treating the packed batch as one sequence must fail the pin."""
+    def bad(q, k, v, do, cu_q, cu_k, scale, causal):
+        gq, gk, gv = oracle.attention_bwd(q[None], k[None], v[None], do[None], scale, causal)
+        return gq[0], gk[0], gv[0]
+    with pytest.raises(AssertionError):
+        _varlen_fd(bad, True, 501)
