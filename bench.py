@@ -130,6 +130,7 @@ def run_config(n, args, dev):
     (the parity-test configurations) and print one JSON line for it."""
     import torch
     import workloads as wl
+    import numpy as np
     import exact_tiled_attention_11_amd as fa
     w = wl.CFG[n]
     log("generating inputs for %s" % w.name)
@@ -163,6 +164,19 @@ def run_config(n, args, dev):
                                          alibi_slopes=sd, out=o, lse=lse)
         else:
             call = lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    elif w.kind == "varlen" and w.backward:
+        q, k, v, cu = wl.varlen_inputs(w)
+        q, k, v = q.to(dev), k.to(dev), v.to(dev)
+        do = wl.tensor(w, 3, tuple(q.shape)).to(dev)
+        cud = torch.from_numpy(cu).to(dev)
+        mx = int(np.diff(cu).max())
+        o, lse = fa.fwd_varlen(q, k, v, cud, cud, causal=w.causal, scale=w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(1, w.H, q.shape[0]), dtype=torch.uint8,
+                         device=dev)
+        call = lambda: fa.bwd_varlen(q, k, v, o, lse, do, cud, cud, causal=w.causal,
+                                     scale=w.scale, max_seqlen_q=mx, max_seqlen_k=mx, dq=dq,
+                                     dk=dk, dv=dv, workspace=ws)
     elif w.kind == "varlen":
         q, k, v, cu = wl.varlen_inputs(w)
         q, k, v = q.to(dev), k.to(dev), v.to(dev)
@@ -235,14 +249,14 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
-    ap.add_argument("--config", type=int, choices=list(range(1, 14)), default=None,
+    ap.add_argument("--config", type=int, choices=list(range(1, 15)), default=None,
                     help="time one workload alone (its library call only) and print a JSON "
                          "line for it instead of the bench line: 1-5 the benchmark table, "
                          "6 its decode over a paged cache, 7 / 8 its N8192 causal prefill "
                          "with a 2048-key prefix mask / with ALiBi, 9 the gradients of "
                          "that prefill (fa_bwd), 10 / 11 that prefill / its gradients with "
                          "attention dropout 0.1, 12 / 13 the gradients with the prefix mask / "
-                         "with ALiBi")
+                         "with ALiBi, 14 the gradients of the varlen workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "

@@ -27,9 +27,10 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
     "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_masked", "fa_bwd_dropout",
+    "fa_bwd_varlen",
     "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
-    "fwd", "fwd_masked", "fwd_dropout", "bwd", "fwd_varlen", "decode_splitkv",
+    "fwd", "fwd_masked", "fwd_dropout", "bwd", "fwd_varlen", "bwd_varlen", "decode_splitkv",
     "decode_splitkv_paged",
 ]
 
@@ -51,6 +52,8 @@ _SIGS = {
                             _i, _vp, _f, _u64, _vp, _sz, _i, _vp]),
     "fa_bwd_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                            _i, _vp, _i, _vp, _vp, _sz, _i, _vp]),
+    "fa_bwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                           _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _vp, _sz, _i, _vp]),
@@ -128,6 +131,14 @@ def fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, cau
     return load().fa_bwd_masked(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal,
                                 seqlens_k, prefix, alibi_slopes, workspace, workspace_bytes, dtype,
                                 stream)
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
+                  total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal, workspace,
+                  workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
+                                nseq, total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale,
+                                causal, workspace, workspace_bytes, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, Nq) -> int:
@@ -351,6 +362,40 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
                        _stream(stream))
     _check("fa_fwd_varlen", st)
     return out, lse
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
+               scale: Optional[float] = None, max_seqlen_q: Optional[int] = None,
+               max_seqlen_k: Optional[int] = None, dq=None, dk=None, dv=None, workspace=None,
+               stream=None) -> Tuple:
+    """Gradients for fwd_varlen (packed q [total_q, H, D], k, v [total_k, H, D], lse [H, total_q]).
+    max_seqlen_q / max_seqlen_k default to the longest ranges of cu_seqlens (read on the host:
+    pass them to avoid that synchronisation)."""
+    import torch
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_seqlen_q is None:
+        max_seqlen_q = int(torch.diff(cu_seqlens_q).max().item()) if nseq > 0 else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int(torch.diff(cu_seqlens_k).max().item()) if nseq > 0 else 0
+    dq = torch.zeros_like(q) if dq is None else dq
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(1, H, total_q), 16), dtype=torch.uint8,
+                                device=q.device)
+    st = fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                       _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq, total_q,
+                       total_k, int(max_seqlen_q), int(max_seqlen_k), H, D, float(scale),
+                       int(bool(causal)), _ptr(workspace), workspace.numel(), _dtype_code(q),
+                       _stream(stream))
+    _check("fa_bwd_varlen", st)
+    return dq, dk, dv
 
 
 def decode_splitkv(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = None,

@@ -263,6 +263,66 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
 
 extern "C" {
 
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                          int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int H,
+                          int D, float scale, int causal, void* workspace, size_t workspace_bytes,
+                          fa_dtype_t dtype, void* stream) {
+  if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit only
+  if (nseq < 1 || H < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!cu_seqlens_q || !cu_seqlens_k || ((uintptr_t)cu_seqlens_q & 3u) != 0 ||
+      ((uintptr_t)cu_seqlens_k & 3u) != 0)
+    return FA_ERR_INVALID_ARG;
+  if (total_q == 0 && total_k == 0) return FA_OK;
+  if ((total_q > 0 && (!q || !o || !lse || !dout || !dq)) ||
+      (total_k > 0 && (!k || !v || !dk || !dv)))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  const long long rows = fa::bwd_block_rows();
+  const long long nsh = (long long)nseq * H;
+  if (((long long)max_seqlen_q + rows - 1) / rows * nsh > 0x7fffffffLL ||
+      ((long long)max_seqlen_k + rows - 1) / rows * nsh > 0x7fffffffLL)
+    return FA_ERR_INVALID_ARG;
+  if ((long long)total_q * H > 0x7fffffffLL * 256LL) return FA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(1, H, total_q)) return FA_ERR_WORKSPACE;
+
+  fa_status_t st = device_ok();
+  if (st != FA_OK) return st;
+
+  fa::BwdArgs a = {};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = (float*)workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = nseq;
+  a.H = H;
+  a.Nq = max_seqlen_q;
+  a.Nk = max_seqlen_k;
+  a.nqb = (int)((max_seqlen_q + rows - 1) / rows);
+  a.c = fmaxf(scale * kLog2eF, 1e-30f);
+  a.scale = scale;
+  a.drop_scale = 1.f;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return from_hip(fa::launch_bwd(a, dtype, D, causal != 0, (hipStream_t)stream));
+}
+
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
   if (nseq < 1 || total_q < 0) return 0;
   // the smallest query block of any instance bounds the tile count from above

@@ -35,6 +35,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "launch.h"
 
@@ -149,25 +151,70 @@ __device__ __forceinline__ frag tr_frag(const FA_LDS(char)* tile, int off, int t
   return __builtin_bit_cast(frag, u);
 }
 
+// The (batch or sequence, head, block) of a workgroup: grid index = block
+// level * (B * H) + batch * H + head.  For a packed batch, sequence b owns
+// rows cu[b] .. cu[b+1] of the packed tensors (clamped to the totals, as in
+// the forward).
+struct BwdItem {
+  int b, h, blk, lq, lk;
+  long long q_tok0, k_tok0;  // first token row of the queries / keys
+  long long stat0;           // lse / delta index of query row 0
+  int kwrite;                // keys whose dK / dV rows this item writes
+};
+template <bool VARLEN>
+__device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a) {
+  BwdItem w;
+  const int nbh = a.B * a.H;
+  w.blk = blockIdx.x / nbh;
+  const int bh = blockIdx.x - w.blk * nbh;
+  w.b = bh / a.H;
+  w.h = bh - w.b * a.H;
+  if constexpr (!VARLEN) {
+    w.lq = a.Nq;
+    w.lk = a.seqlens_k ? min(max(a.seqlens_k[w.b], 0), a.Nk) : a.Nk;
+    w.q_tok0 = (long long)w.b * a.Nq;
+    w.k_tok0 = (long long)w.b * a.Nk;
+    w.stat0 = ((long long)w.b * a.H + w.h) * a.Nq;
+    w.kwrite = a.Nk;  // padding keys get zero rows
+  } else {
+    const int q0 = min(max(a.cu_q[w.b], 0), a.total_q);
+    const int q1 = min(max(a.cu_q[w.b + 1], q0), a.total_q);
+    const int k0 = min(max(a.cu_k[w.b], 0), a.total_k);
+    const int k1 = min(max(a.cu_k[w.b + 1], k0), a.total_k);
+    w.lq = q1 - q0;
+    w.lk = k1 - k0;
+    w.q_tok0 = q0;
+    w.k_tok0 = k0;
+    w.stat0 = (long long)w.h * a.total_q + q0;
+    w.kwrite = w.lk;
+  }
+  return w;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// delta[b, h, i] = sum_d dO[b, i, h, d] * O[b, i, h, d]
+// delta = rowsum(dO o O) for every (query row, head), in lse's layout
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
-  const long long row = (long long)blockIdx.x * 256 + threadIdx.x;  // (b, i, h), h fastest
-  if (row >= (long long)a.B * a.Nq * a.H) return;
+  const long long row = (long long)blockIdx.x * 256 + threadIdx.x;  // (token, head), head fastest
+  const long long ntok = VARLEN ? (long long)a.total_q : (long long)a.B * a.Nq;
+  if (row >= ntok * a.H) return;
   const int h = (int)(row % a.H);
-  const long long bi = row / a.H;
-  const int i = (int)(bi % a.Nq);
-  const int b = (int)(bi / a.Nq);
+  const long long tok = row / a.H;
   const u32x4_t* po = (const u32x4_t*)((const T*)a.o + row * D);
   const u32x4_t* pd = (const u32x4_t*)((const T*)a.dout + row * D);
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 8; ++c) s += dot8_16<T>(po[c], pd[c]);
-  a.delta[((long long)b * a.H + h) * a.Nq + i] = s;
+  if constexpr (VARLEN) {
+    a.delta[(long long)h * a.total_q + tok] = s;
+  } else {
+    const int i = (int)(tok % a.Nq);
+    const int b = (int)(tok / a.Nq);
+    a.delta[((long long)b * a.H + h) * a.Nq + i] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -178,7 +225,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 constexpr int kTrRow = 36;
 constexpr int kTrWave = 32 * kTrRow;
 
-template <typename T, int D, bool CAUSAL, int MODE>
+template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
 __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
   using E = Elem<T>;
@@ -195,29 +242,28 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   FA_LDS(uint8_t)* trb = (FA_LDS(uint8_t)*)trbuf_raw + (DROP ? wave * kTrWave : 0);
 
-  const int nbh = a.B * a.H;
-  const int kblk = blockIdx.x / nbh;  // ascending: causal key blocks with most queries first
-  const int bh = blockIdx.x - kblk * nbh;
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int lq = a.Nq;
-  const int lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.Nk) : a.Nk;
+  // key blocks ascending: causal key blocks with most queries first
+  const BwdItem wi = bwd_item<VARLEN>(a);
+  const int b = wi.b, h = wi.h;
+  const int lq = wi.lq, lk = wi.lk;
   const int off = lk - lq;
-  const int k0 = kblk * kNW * kRows;
+  const int k0 = wi.blk * kNW * kRows;
+  if (VARLEN && k0 >= lk) return;  // past this sequence's keys: nothing to write
   const int kw0 = k0 + wave * kRows;  // this wave's first key
   const int n = kw0 + col;             // this lane's key
 
   const size_t rs = (size_t)a.H * D;
-  const T* qb = (const T*)a.q + (size_t)b * a.Nq * rs + (size_t)h * D;
-  const T* dob = (const T*)a.dout + (size_t)b * a.Nq * rs + (size_t)h * D;
-  const float* lseb = a.lse + ((size_t)b * a.H + h) * a.Nq;
-  const float* dlb = a.delta + ((size_t)b * a.H + h) * a.Nq;
+  const T* qb = (const T*)a.q + (size_t)wi.q_tok0 * rs + (size_t)h * D;
+  const T* dob = (const T*)a.dout + (size_t)wi.q_tok0 * rs + (size_t)h * D;
+  const float* lseb = a.lse + wi.stat0;
+  const float* dlb = a.delta + wi.stat0;
 
   // K and V rows of this lane's key (B operands), zero past the real keys
   frag kf[KS], vf[KS];
   {
     const bool ok = n < lk;
-    const T* kr = (const T*)a.k + ((size_t)b * a.Nk + (ok ? n : 0)) * rs + (size_t)h * D;
-    const T* vr = (const T*)a.v + ((size_t)b * a.Nk + (ok ? n : 0)) * rs + (size_t)h * D;
+    const T* kr = (const T*)a.k + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs + (size_t)h * D;
+    const T* vr = (const T*)a.v + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs + (size_t)h * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       frag z = {};
@@ -382,9 +428,9 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
   // dK = scale * dK^T, dV = dV^T (times 1 / (1 - p) with dropout) for keys
   // < Nk (padding keys: zero)
   const float vsc = DROP ? a.drop_scale : 1.f;
-  if (n < a.Nk) {
-    T* dkr = (T*)a.dk + ((size_t)b * a.Nk + n) * rs + (size_t)h * D;
-    T* dvr = (T*)a.dv + ((size_t)b * a.Nk + n) * rs + (size_t)h * D;
+  if (n < wi.kwrite) {
+    T* dkr = (T*)a.dk + ((size_t)wi.k_tok0 + n) * rs + (size_t)h * D;
+    T* dvr = (T*)a.dv + ((size_t)wi.k_tok0 + n) * rs + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -407,7 +453,7 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 // ---------------------------------------------------------------------------
 // (four waves per SIMD fit the causal head_dim-64 instance without spills,
 // measured 1 % faster; the others keep the compiler's choice)
-template <typename T, int D, bool CAUSAL, int MODE>
+template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
 __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
   using E = Elem<T>;
@@ -422,29 +468,27 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  const int nbh = a.B * a.H;
-  const int level = blockIdx.x / nbh;
-  const int bh = blockIdx.x - level * nbh;
-  const int qblk = CAUSAL ? (a.nqb - 1 - level) : level;  // causal: longest first
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int lq = a.Nq;
-  const int lk = a.seqlens_k ? min(max(a.seqlens_k[b], 0), a.Nk) : a.Nk;
+  const BwdItem wi = bwd_item<VARLEN>(a);
+  const int qblk = CAUSAL ? (a.nqb - 1 - wi.blk) : wi.blk;  // causal: longest first
+  const int b = wi.b, h = wi.h;
+  const int lq = wi.lq, lk = wi.lk;
   const int off = lk - lq;
   const int q0 = qblk * kNW * kRows;
+  if (VARLEN && q0 >= lq) return;  // past this sequence's rows: nothing to write
   const int wq0 = q0 + wave * kRows;
   const int qi = wq0 + col;  // this lane's query row
   const int wq_last = min(wq0 + kRows, lq) - 1;
 
   const size_t rs = (size_t)a.H * D;
-  const T* kb = (const T*)a.k + (size_t)b * a.Nk * rs + (size_t)h * D;
-  const T* vb = (const T*)a.v + (size_t)b * a.Nk * rs + (size_t)h * D;
+  const T* kb = (const T*)a.k + (size_t)wi.k_tok0 * rs + (size_t)h * D;
+  const T* vb = (const T*)a.v + (size_t)wi.k_tok0 * rs + (size_t)h * D;
 
   // Q and dO rows of this lane's query (B operands), lse and delta
   frag qf[KS], dof[KS];
   float lrow = INFINITY, drow = 0.f;
   {
     const bool ok = qi < lq;
-    const size_t ro = ((size_t)b * a.Nq + (ok ? qi : 0)) * rs + (size_t)h * D;
+    const size_t ro = ((size_t)wi.q_tok0 + (ok ? qi : 0)) * rs + (size_t)h * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       frag z = {};
@@ -452,9 +496,9 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
       dof[ks] = ok ? *(const frag*)((const T*)a.dout + ro + ks * 16 + hh * 8) : z;
     }
     if (ok) {
-      const float l = a.lse[((size_t)b * a.H + h) * a.Nq + qi];
+      const float l = a.lse[wi.stat0 + qi];
       lrow = l == -INFINITY ? INFINITY : l * kLog2e;
-      drow = a.delta[((size_t)b * a.H + h) * a.Nq + qi];
+      drow = a.delta[wi.stat0 + qi];
     }
   }
   f32x16_t dqa[DB];
@@ -557,7 +601,7 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
   }
 
   if (qi < lq) {
-    T* dqr = (T*)a.dq + ((size_t)b * a.Nq + qi) * rs + (size_t)h * D;
+    T* dqr = (T*)a.dq + ((size_t)wi.q_tok0 + qi) * rs + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -578,33 +622,40 @@ template <typename T, int D>
 static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t stream) {
   // empty grids (no queries or no keys) are skipped: the other kernel still
   // writes the zero gradients of its side
-  const long long rows = (long long)a.B * a.Nq * a.H;
-  if (rows > 0)
-    hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       stream, a);
+  const bool varlen = a.cu_q != nullptr;
+  const long long rows = (varlen ? (long long)a.total_q : (long long)a.B * a.Nq) * a.H;
+  if (rows > 0) {
+    const dim3 grid((unsigned)((rows + 255) / 256));
+    if (varlen) hipLaunchKernelGGL((bwd_delta_kernel<T, D, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_delta_kernel<T, D, false>), grid, dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned nbh = (unsigned)(a.B * a.H);
   const unsigned gk = (unsigned)((a.Nk + kNW * kRows - 1) / (kNW * kRows)) * nbh;
   const unsigned gq = (unsigned)a.nqb * nbh;
   const int mode = a.drop_t ? kBwdDrop : (a.alibi ? kBwdAlibi : kBwdPlain);
-  auto launch2 = [&](auto mc) {
+  auto launch2 = [&](auto mc, auto vc) {
     constexpr int M = decltype(mc)::value;
+    constexpr bool V = decltype(vc)::value;
     if (gk > 0) {
-      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, M>), dim3(gk), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, M>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, M, V>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, M, V>), dim3(gk), dim3(kNW * 64), 0, stream, a);
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
     }
     if (gq > 0) {
-      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, M>), dim3(gq), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, M>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+      if (causal) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, M, V>), dim3(gq), dim3(kNW * 64), 0, stream, a);
+      else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, M, V>), dim3(gq), dim3(kNW * 64), 0, stream, a);
     }
     return hipGetLastError();
   };
-  if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{});
-  if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{});
-  return launch2(std::integral_constant<int, kBwdPlain>{});
+  using F = std::false_type;
+  // packed batches: plain mode only (the entry point checks)
+  if (varlen) return launch2(std::integral_constant<int, kBwdPlain>{}, std::true_type{});
+  if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{}, F{});
+  if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{}, F{});
+  return launch2(std::integral_constant<int, kBwdPlain>{}, F{});
 }
 
 int bwd_block_rows() { return kNW * kRows; }

@@ -103,6 +103,12 @@ struct BwdArgs {
   // mask families of the forward being differentiated (zero / null: none)
   int prefix;              // with causal: keys [0, prefix) are seen by every query
   const float* alibi;      // [H] slopes: score += -slope_h * |j - (i + Lk - Lq)|
+  // packed variable-length batches (cu_q null: fixed length).  Then B is the
+  // number of sequences, Nq / Nk the longest query / key lengths, lse and
+  // delta are [H, total_q] and the tensors [total, H, D].
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
 };
 
 int bwd_block_rows();

@@ -198,6 +198,30 @@ FA355_API fa_status_t fa_bwd(const void* q, const void* k, const void* v, const 
                              fa_dtype_t dtype, void* stream);
 
 /*
+ * Backward pass of fa_fwd_varlen (packed variable-length batches): the
+ * gradients of each sequence's own attention, for the o and lse that
+ * fa_fwd_varlen wrote with the same cu_seqlens, scale and causal.
+ *   q, o, dout, dq: [total_q, H, D];  k, v, dk, dv: [total_k, H, D]; fp16 or
+ *       bf16 (fp32: FA_ERR_UNSUPPORTED)
+ *   lse: [H, total_q] float32 from fa_fwd_varlen
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [nseq + 1], as fa_fwd_varlen
+ *       (each range clamped to [0, total])
+ *   max_seqlen_q, max_seqlen_k: at least the longest query / key range (they
+ *       size the grid; rows past them are not computed)
+ *   workspace: at least fa_bwd_workspace_bytes(1, H, total_q) bytes
+ * dq rows and dk / dv rows that belong to a sequence are written; rows
+ * outside every range are left untouched.  Ordering, reproducibility and
+ * errors as fa_bwd.
+ */
+FA355_API fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk,
+                                    void* dv, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                    int total_k, int max_seqlen_q, int max_seqlen_k, int H, int D,
+                                    float scale, int causal, void* workspace,
+                                    size_t workspace_bytes, fa_dtype_t dtype, void* stream);
+
+/*
  * Backward pass of fa_fwd_masked: as fa_bwd, for the o and lse that
  * fa_fwd_masked wrote with the same prefix and alibi_slopes (prefix mask:
  * with causal only, keys [0, prefix) are seen by every query; ALiBi: score

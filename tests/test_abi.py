@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
-        "fa_bwd", "fa_bwd_dropout", "fa_bwd_masked", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
+        "fa_bwd", "fa_bwd_dropout", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_workspace_bytes",
+        "fa_fwd_dropout",
         "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
@@ -266,3 +267,27 @@ def test_bwd_masked_validation():
     assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(Nq=0, Nk=0) == fa.FA_OK
+
+
+def test_bwd_varlen_validation():
+    base = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cq=P, ck=P, nseq=3, tq=100, tk=120,
+                mq=50, mk=60, H=2, D=128, scale=0.1, causal=1, ws=P, wsb=1 << 20,
+                dtype=fa.FA_F16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                a["dv"], a["cq"], a["ck"], a["nseq"], a["tq"], a["tk"], a["mq"],
+                                a["mk"], a["H"], a["D"], a["scale"], a["causal"], a["ws"],
+                                a["wsb"], a["dtype"], a["stream"])
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert call(D=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(nseq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(mq=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(cq=None) == fa.FA_ERR_INVALID_ARG
+    assert call(ck=P + 2) == fa.FA_ERR_INVALID_ARG             # int32 offsets not 4-byte aligned
+    assert call(dq=MIS) == fa.FA_ERR_INVALID_ARG
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=fa.fa_bwd_workspace_bytes(1, 2, 100) - 1) == fa.FA_ERR_WORKSPACE
+    assert call(tq=0, tk=0) == fa.FA_OK

@@ -155,3 +155,53 @@ MASKED_BWD = [
                          ids=lambda x: getattr(x, "name", str(x)))
 def test_bwd_masked(w, prefix, alibi, seqlens):
     masked_bwd_case(w, prefix, alibi, seqlens)
+
+
+def varlen_bwd_case(name, dtype, D, H, causal, lens_q, lens_k, seed):
+    """fa_fwd_varlen then fa_bwd_varlen against the oracle's packed backward."""
+    import exact_tiled_attention_11_amd as fa
+    fa.load()
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    w = wl.Workload(name, "varlen", dtype, H=H, D=D, causal=causal, scale=1 / math.sqrt(D), seed=seed)
+    q = wl.tensor(w, 0, (int(cu_q[-1]), H, D))
+    k = wl.tensor(w, 1, (int(cu_k[-1]), H, D))
+    v = wl.tensor(w, 2, (int(cu_k[-1]), H, D))
+    do = wl.tensor(w, 3, (int(cu_q[-1]), H, D))
+    cqd, ckd = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    say("  fa_fwd_varlen + fa_bwd_varlen %s" % name)
+    o, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, causal=causal, scale=w.scale)
+    outs = []
+    for rep in range(2):
+        dq = torch.full_like(qd, float("nan"))
+        dk = torch.full_like(kd, float("nan"))
+        dv = torch.full_like(vd, float("nan"))
+        fa.bwd_varlen(qd, kd, vd, o, lse, dod, cqd, ckd, causal=causal, scale=w.scale,
+                      max_seqlen_q=int(max(lens_q)), max_seqlen_k=int(max(lens_k)), dq=dq, dk=dk,
+                      dv=dv)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+    dq, dk, dv = outs[0]
+    rq, rk, rv = oracle.attention_varlen_bwd(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), wl.to_f64(do),
+                                             cu_q, cu_k, w.scale, causal)
+    assert_grad_close(dtype, wl.to_f64(dq), rq, "%s dq" % name)
+    assert_grad_close(dtype, wl.to_f64(dk), rk, "%s dk" % name)
+    assert_grad_close(dtype, wl.to_f64(dv), rv, "%s dv" % name)
+
+
+VARLEN_BWD = [
+    ("f16 D128 causal H2 5 seqs (one empty)", "f16", 128, 2, True, [300, 0, 129, 1, 450],
+     [300, 0, 129, 1, 450], 71),
+    ("bf16 D64 causal H3 Lq != Lk", "bf16", 64, 3, True, [100, 260, 33], [300, 130, 33], 72),
+    ("bf16 D64 bidirectional H2 Lq != Lk", "bf16", 64, 2, False, [64, 200, 5], [190, 7, 128], 73),
+    ("f16 D64 causal H4 8 short seqs", "f16", 64, 4, True, [17, 31, 32, 33, 63, 64, 65, 2],
+     [17, 31, 32, 33, 63, 64, 65, 2], 74),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_BWD, ids=lambda c: c[0])
+def test_bwd_varlen(case):
+    varlen_bwd_case(*case)

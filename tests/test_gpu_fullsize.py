@@ -399,3 +399,37 @@ def test_bwd_masked_full_size_heads(cfg):
                                           alibi_slopes=None if slopes is None else slopes[h:h + 1])
         for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
             assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref, "%s %s b%d h%d" % (w.name, name, b, h))
+
+
+def test_bwd_varlen_full_size_sampled():
+    """Gradients of the packed varlen workload (bench.py --config 14): reruns
+    bit-identical, finite, and the shortest sequence (two heads) against the
+    oracle's backward of that sequence alone."""
+    fa = _fa()
+    w = wl.CFG[14]
+    say("generate %s" % w.name)
+    q, k, v, cu = wl.varlen_inputs(w)
+    do = wl.tensor(w, 3, tuple(q.shape))
+    cud = torch.from_numpy(cu).cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    lens = np.diff(cu)
+    mx = int(lens.max())
+    say("fa_fwd_varlen + fa_bwd_varlen %s" % w.name)
+    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, causal=True, scale=w.scale)
+    g1 = fa.bwd_varlen(qd, kd, vd, o, lse, dod, cud, cud, causal=True, scale=w.scale, max_seqlen_q=mx,
+                       max_seqlen_k=mx)
+    g2 = fa.bwd_varlen(qd, kd, vd, o, lse, dod, cud, cud, causal=True, scale=w.scale, max_seqlen_q=mx,
+                       max_seqlen_k=mx)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
+        assert torch.isfinite(a).all().item()
+    dq, dk, dv = (t.cpu() for t in g1)
+    s = int(np.argmin(lens))
+    a0, a1 = int(cu[s]), int(cu[s + 1])
+    for h in (0, w.H - 1):
+        sl = (slice(a0, a1), slice(h, h + 1))
+        rq, rk, rv = oracle.attention_bwd(wl.to_f64(q[sl])[None], wl.to_f64(k[sl])[None],
+                                          wl.to_f64(v[sl])[None], wl.to_f64(do[sl])[None], w.scale, True)
+        for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            assert_grad_close(w.dtype, wl.to_f64(got[sl]), ref[0], "%s %s seq%d h%d" % (w.name, name, s, h))

@@ -154,6 +154,10 @@ CFG[11] = replace(CFG[9], name="backward causal bf16 B4 H16 N8192 D64 dropout 0.
 CFG[12] = replace(CFG[7], name="backward causal bf16 B4 H16 N8192 D64 prefix 2048", backward=True)
 CFG[13] = replace(CFG[8], name="backward causal bf16 B4 H16 N8192 D64 ALiBi", backward=True)
 
+# Beyond the table: the gradients of the packed varlen prefill.
+CFG[14] = replace(CFG[4], name="backward varlen causal fp16 8 seqs U[1024,16384] H32 D128",
+                  backward=True)
+
 # Beyond the table: the decode workload over a paged cache (16-row pages at
 # shuffled pool positions), the cache layout of serving runtimes.
 CFG[6] = replace(CFG[5], name="paged decode bf16 B64 H32 D128 Lk U[4096,32768] chunk 256 page 16",
