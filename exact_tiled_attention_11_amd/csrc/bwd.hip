@@ -18,6 +18,8 @@
 //    with the chunk's queries along the registers, so P and dS are packed in
 //    place as the B operand of dV^T += dO^T P and dK^T += Q^T dS, whose A
 //    operands are transposing reads (ds_read_b64_tr_b16) of the same LDS tiles.
+//    At head_dim 128 a pair of waves shares each 32 keys instead (one computes
+//    P and dV, the other dP, dS and dK, a chunk behind; bwd_dkdv_split_kernel).
 //  * dQ: one workgroup per 128 query rows (a wave per 32), Q and dO in
 //    VGPRs, 32-key blocks of K and V streaming through LDS; lanes own query
 //    columns, as in the forward kernel, and dQ^T += K^T dS^T.
@@ -52,8 +54,10 @@ constexpr int kBwdPlain = 0, kBwdAlibi = 1, kBwdDrop = 2;
 constexpr int kRows = 32;  // rows per wave and per streamed tile
 
 // LDS position (16-byte chunks) of chunk c of tile row r: the XOR pattern of
-// the forward kernel, conflict-free for 8-row column reads and for the
-// 4-row x 32-byte transposing reads.
+// the forward kernel, conflict-free for the 4-row x 32-byte transposing
+// reads (the 16-byte row reads of head_dim 128 and of 16 rows at head_dim 64
+// meet 2-way conflicts; conflict-free patterns need a per-lane offset for the
+// transposing read 8 rows down and measured slower).
 __device__ __forceinline__ int bswz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 template <typename T>
@@ -74,41 +78,61 @@ __device__ __forceinline__ float dot8_16(const u32x4_t& x, const u32x4_t& y) {
 }
 
 // Two 32-row tiles (rows x D) staged global -> VGPRs -> LDS by the whole
-// workgroup: each thread moves kPer 16-byte chunks of each tile.
-template <typename T, int D>
+// workgroup of NT threads: each thread moves kPer 16-byte chunks of each
+// tile, or, when the two tiles hold one chunk per thread, one chunk of one
+// of them.
+template <typename T, int D, int NT = kNW * 64>
 struct TilePair {
-  static constexpr int kCPR = D / 8;                      // 16-byte chunks per row
-  static constexpr int kRB = D * 2;                       // bytes per row
+  static constexpr int kCPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int kRB = D * 2;                  // bytes per row
   static constexpr int kTileB = kRows * kRB;
-  static constexpr int kPer = kRows * kCPR / (kNW * 64);  // chunks per thread per tile
-  u32x4_t a[kPer], b[kPer];
+  static constexpr int kChunks = kRows * kCPR;       // chunks per tile
+  static constexpr bool kOne = 2 * kChunks == NT;    // one chunk per thread in all
+  static constexpr int kPer = kOne ? 1 : kChunks / NT;  // chunks per thread per tile
+  static_assert(kOne || (kPer >= 1 && kPer * NT == kChunks), "whole chunks per thread");
+  u32x4_t a[kPer], b[kOne ? 1 : kPer];
 
   // rows row0 .. row0+31 of the two tensors (token stride rs elements),
   // rows >= nrows read as zero
   __device__ __forceinline__ void load(const T* pa, const T* pb, size_t rs, int row0, int nrows,
                                        int tid) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int p = tid + u * kNW * 64;
+    if constexpr (kOne) {
+      const int p = tid % kChunks;
       const int r = p / kCPR, c = p % kCPR;
       const int row = row0 + r;
-      if (row < nrows) {
-        a[u] = *(const u32x4_t*)(pa + (size_t)row * rs + c * 8);
-        b[u] = *(const u32x4_t*)(pb + (size_t)row * rs + c * 8);
-      } else {
-        a[u] = u32x4_t{};
-        b[u] = u32x4_t{};
+      const T* src = tid < kChunks ? pa : pb;
+      a[0] = row < nrows ? *(const u32x4_t*)(src + (size_t)row * rs + c * 8) : u32x4_t{};
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int p = tid + u * NT;
+        const int r = p / kCPR, c = p % kCPR;
+        const int row = row0 + r;
+        if (row < nrows) {
+          a[u] = *(const u32x4_t*)(pa + (size_t)row * rs + c * 8);
+          b[u] = *(const u32x4_t*)(pb + (size_t)row * rs + c * 8);
+        } else {
+          a[u] = u32x4_t{};
+          b[u] = u32x4_t{};
+        }
       }
     }
   }
   __device__ __forceinline__ void store(FA_LDS(char)* ta, FA_LDS(char)* tb, int tid) const {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int p = tid + u * kNW * 64;
+    if constexpr (kOne) {
+      const int p = tid % kChunks;
       const int r = p / kCPR, c = p % kCPR;
       const int pos = r * kRB + ((c ^ bswz(r)) * 16);
-      *(FA_LDS(u32x4_t)*)(ta + pos) = a[u];
-      *(FA_LDS(u32x4_t)*)(tb + pos) = b[u];
+      *(FA_LDS(u32x4_t)*)((tid < kChunks ? ta : tb) + pos) = a[0];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int p = tid + u * NT;
+        const int r = p / kCPR, c = p % kCPR;
+        const int pos = r * kRB + ((c ^ bswz(r)) * 16);
+        *(FA_LDS(u32x4_t)*)(ta + pos) = a[u];
+        *(FA_LDS(u32x4_t)*)(tb + pos) = b[u];
+      }
     }
   }
 };
@@ -225,6 +249,51 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
 constexpr int kTrRow = 36;
 constexpr int kTrWave = 32 * kTrRow;
 
+// Keep words of a lane of the dK/dV kernels, where lanes are keys: the lane
+// draws the Philox call of query q0 + col for keys kw0 + 16 hh .. +15 and
+// stores the bytes at [key][query] in the wave's LDS tile; word g then holds
+// the bytes of its own key for the chunk's query rows 8g + 4hh .. +3.
+__device__ __forceinline__ void dkdv_keep_words(uint32_t kw[4], FA_LDS(uint8_t)* trb, int kw0,
+                                                int q0, int col, int hh, int h, int b,
+                                                const BwdArgs& a) {
+  const Philox4 x = philox4x32_10((uint32_t)((kw0 >> 4) + hh), (uint32_t)(q0 + col), (uint32_t)h,
+                                  (uint32_t)b, a.seed_lo, a.seed_hi);
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+    trb[(16 * hh + m) * kTrRow + col] = (uint8_t)(x.w[m >> 2] >> (8 * (m & 3)));
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    kw[g] = *(const FA_LDS(uint32_t)*)(trb + col * kTrRow + 8 * g + 4 * hh);
+}
+
+// exp2 exponents of the 16 (query row, key) pairs of a lane of the dK/dV
+// kernels: register r holds row 8(r>>2) + 4hh + (r&3) of the chunk, the key
+// is n.  Query row m sees the key iff m >= lim (and the key is real); the
+// key's distance to that row's own position is lim - m.  On a masked chunk a
+// hidden pair's exponent is clamped to -2^99 or less (probability exactly
+// 0): row cr is visible iff cr >= limv, tested as min(x, (cr - limv + 1/2)
+// 2^100), exact for |limv| < 2^20.
+template <bool CAUSAL, bool ALIBI>
+__device__ __forceinline__ void dkdv_exponents(float x[16], const f32x16_t& s, const float lr[16],
+                                               const BwdArgs& a, float slope2, bool masked,
+                                               int lim, int n, int lk) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], a.c, -lr[r]);
+  if constexpr (ALIBI) {  // - slope |key - (row + Lk - Lq)|
+    const float fl = (float)lim;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      x[r] = __builtin_fmaf(-slope2, fabsf(fl - (float)(8 * (r >> 2) + (r & 3))), x[r]);
+  }
+  if (masked) {
+    const int limv = n < lk ? (CAUSAL && n >= a.prefix ? lim : -(1 << 20)) : (1 << 20);
+    const float base = (0.5f - (float)limv) * 0x1p100f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      x[r] = fminf(x[r], base + (float)(8 * (r >> 2) + (r & 3)) * 0x1p100f);
+  }
+}
+
 template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
 __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
@@ -339,43 +408,11 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
     }
     const bool masked =
         (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > max(q0 + off, pre));
-    // query row m of the chunk sees this lane's key iff m >= lim (and the key is
-    // real); the key's distance to that row's own position is lim - m
     const int lim = n - q0 - off - 4 * hh;
     uint32_t kw[4];
-    if constexpr (DROP) {
-      // this lane draws the bytes of keys kw0 + 16*hh .. +15 for query q0 + col
-      // and stores them at [key][query]; then reads the bytes of its own key
-      // for its queries 8g + 4hh .. +3 (word g of register group g)
-      const Philox4 x = philox4x32_10((uint32_t)((kw0 >> 4) + hh), (uint32_t)(q0 + col),
-                                      (uint32_t)h, (uint32_t)b, a.seed_lo, a.seed_hi);
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        trb[(16 * hh + m) * kTrRow + col] = (uint8_t)(x.w[m >> 2] >> (8 * (m & 3)));
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        kw[g] = *(const FA_LDS(uint32_t)*)(trb + col * kTrRow + 8 * g + 4 * hh);
-    }
-    // exponents; on a masked chunk a hidden pair's exponent is clamped to
-    // -2^99 or less (probability exactly 0): row cr is visible iff cr >= limv,
-    // tested as min(x, (cr - limv + 1/2) 2^100), exact for |limv| < 2^20
+    if constexpr (DROP) dkdv_keep_words(kw, trb, kw0, q0, col, hh, h, b, a);
     float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(s[r], a.c, -lr[r]);
-    if constexpr (ALIBI) {  // - slope |key - (row + Lk - Lq)|
-      const float fl = (float)lim;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        x[r] = __builtin_fmaf(-slope2, fabsf(fl - (float)(8 * (r >> 2) + (r & 3))), x[r]);
-    }
-    if (masked) {
-      const int limv =
-          n < lk ? (CAUSAL && n >= a.prefix ? lim : -(1 << 20)) : (1 << 20);
-      const float base = (0.5f - (float)limv) * 0x1p100f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        x[r] = fminf(x[r], base + (float)(8 * (r >> 2) + (r & 3)) * 0x1p100f);
-    }
+    dkdv_exponents<CAUSAL, ALIBI>(x, s, lr, a, slope2, masked, lim, n, lk);
     float p[16], pd[16], ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -444,6 +481,262 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
                       pack2(vv[4 * g4 + 2] * vsc, vv[4 * g4 + 3] * vsc, (T*)nullptr)};
         *(u32x2_t*)(dkr + d) = wk;
         *(u32x2_t*)(dvr + d) = wv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV with each 32-key block shared by two waves (head_dim 128)
+// ---------------------------------------------------------------------------
+// One wave holding both accumulators of 32 keys at head_dim 128 (dK^T and
+// dV^T, 128 fp32 registers) next to its K and V operands does not fit the
+// 256 architectural VGPRs, and the accumulators then travel between the VGPR
+// and AGPR files on every chunk.  Here a key block belongs to a pair of waves
+// with one accumulator set each: the P wave holds K, computes S = Q K^T, the
+// probabilities (masks, bias, dropout) and dV^T += dO^T P; the dS wave holds
+// V, computes dP = dO V^T, takes P from the P wave through LDS in fp32 and
+// computes dS = P o (dP - delta) and dK^T += Q^T dS.  The MFMA work is that
+// of one wave doing both, the arithmetic and its order are the same, so the
+// results are identical.  Waves 0-3 are the P waves of key blocks 0-3 and
+// waves 4-7 the dS waves, so that each SIMD runs one of each kind.  With
+// dropout the P wave hands over P with the sign bit set on dropped pairs.
+constexpr int kKB = 4;  // key blocks per workgroup (128 keys, as bwd_dkdv_kernel)
+constexpr int kSplitNW = 2 * kKB;
+
+template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
+__global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArgs a) {
+  constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  using TP = TilePair<T, D, kSplitNW * 64>;
+  constexpr int KS = D / 16, DB = D / 32, TS = 2, RB = D * 2;
+  constexpr int kBufB = 2 * TP::kTileB + 2 * kRows * 4;  // Q, dO, lse, delta
+  typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+  constexpr int kStages = 3;  // chunk c - 1 (dS waves), c (P waves), c + 1 (staged)
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[kStages * kBufB];
+  FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
+  // P of each key block, two chunks: 4 x 64 lanes x 16 bytes (lane-major,
+  // register group g)
+  __shared__ __attribute__((aligned(16))) f32x4_t pbuf_raw[2 * kKB * 4 * 64];
+  __shared__ __attribute__((aligned(16))) char trbuf_raw[DROP ? kKB * kTrWave : 16];
+
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = wave & (kKB - 1);
+  const bool pw = wave < kKB;  // P wave (else dS wave)
+  FA_LDS(f32x4_t)* pex = (FA_LDS(f32x4_t)*)pbuf_raw + kb * 4 * 64 + lane;  // + parity * kPB
+  constexpr int kPB = kKB * 4 * 64;
+  FA_LDS(uint8_t)* trb = (FA_LDS(uint8_t)*)trbuf_raw + (DROP ? kb * kTrWave : 0);
+
+  const BwdItem wi = bwd_item<VARLEN>(a);
+  const int b = wi.b, h = wi.h;
+  const int lq = wi.lq, lk = wi.lk;
+  const int off = lk - lq;
+  const int k0 = wi.blk * kKB * kRows;
+  if (VARLEN && k0 >= lk) return;  // past this sequence's keys: nothing to write
+  const int kw0 = k0 + kb * kRows;  // this wave's first key
+  const int n = kw0 + col;          // this lane's key
+
+  const size_t rs = (size_t)a.H * D;
+  const T* qb = (const T*)a.q + (size_t)wi.q_tok0 * rs + (size_t)h * D;
+  const T* dob = (const T*)a.dout + (size_t)wi.q_tok0 * rs + (size_t)h * D;
+  const float* lseb = a.lse + wi.stat0;
+  const float* dlb = a.delta + wi.stat0;
+
+  // B operand rows of this lane's key: K (P wave) or V (dS wave), zero past
+  // the real keys
+  frag kv[KS];
+  {
+    const bool ok = n < lk;
+    const T* src = (const T*)(pw ? a.k : a.v) + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs +
+                   (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      kv[ks] = ok ? *(const frag*)(src + ks * 16 + hh * 8) : z;
+    }
+  }
+  f32x16_t acc[DB];  // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+
+  const int nch = (lq + kRows - 1) / kRows;
+  int c_begin = 0, c_wave = 0;
+  if (CAUSAL) {
+    c_begin = k0 < a.prefix ? 0 : max(0, k0 - off) / kRows;
+    c_wave = kw0 < a.prefix ? 0 : max(0, kw0 - off) / kRows;
+  }
+  const int pre = a.prefix - 1;
+  const float slope2 = ALIBI ? a.alibi[h] * kLog2e : 0.f;
+  const bool wave_live = kw0 < lk;
+
+  ReadLanes<D> rl;
+  rl.init(lane);
+  TP st;
+  float st_l = 0.f;
+  auto stage_load = [&](int c) {
+    st.load(qb, dob, rs, c * kRows, lq, tid);
+    if (tid < 2 * kRows) {
+      const int i = c * kRows + (tid & 31);
+      if (tid < kRows) {
+        const float l = i < lq ? lseb[i] : -INFINITY;
+        st_l = l == -INFINITY ? INFINITY : l * kLog2e;
+      } else {
+        st_l = i < lq ? dlb[i] : 0.f;
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    FA_LDS(char)* base = smem + buf * kBufB;
+    st.store(base, base + TP::kTileB, tid);
+    if (tid < 2 * kRows) *(FA_LDS(float)*)(base + 2 * TP::kTileB + tid * 4) = st_l;
+  };
+
+  // The dS wave runs one chunk behind its P wave: in step c the P wave
+  // handles chunk c and the dS wave finishes chunk c - 1 (with the P that
+  // was handed over in step c - 1) and computes dP of chunk c, so one
+  // barrier per step orders everything.  Buffers: chunk c in stage
+  // (c - c_begin) % 3, P of chunk c in half (c - c_begin) & 1.
+  if (c_begin < nch) {
+    stage_load(c_begin);
+    stage_store(0);
+  }
+  __syncthreads();
+  if (c_begin + 1 < nch) stage_load(c_begin + 1);
+  // end of step c: stage chunk c + 1 (its stage's last readers ran in step
+  // c - 1), barrier, start loading chunk c + 2
+  auto step_end = [&](int c, int j) {
+    if (c + 1 < nch) stage_store((j + 1) % kStages);
+    __syncthreads();
+    if (c + 2 < nch) stage_load(c + 2);
+  };
+  // the two kinds of wave run separate loops with the same barriers
+  if (pw) {
+    for (int c = c_begin; c <= nch; ++c) {
+      const int j = c - c_begin;
+      const FA_LDS(char)* base = smem + (j % kStages) * kBufB;
+      const FA_LDS(char)* tq = base;
+      const FA_LDS(char)* tdo = base + TP::kTileB;
+      const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * TP::kTileB);
+      if (wave_live && c < nch && c >= c_wave) {
+        const int q0 = c * kRows;
+        f32x16_t sd = {};  // S: query rows along registers
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sd = mma(row_frag<frag>(tq, rl.rowl[ks]), kv[ks], sd);
+        float lr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_t l4 = *(const FA_LDS(f32x4_t)*)(tl + 8 * g + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lr[4 * g + e] = l4[e];
+        }
+        const bool masked =
+            (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > max(q0 + off, pre));
+        const int lim = n - q0 - off - 4 * hh;
+        uint32_t kw[4];
+        if constexpr (DROP) dkdv_keep_words(kw, trb, kw0, q0, col, hh, h, b, a);
+        float x[16];
+        dkdv_exponents<CAUSAL, ALIBI>(x, sd, lr, a, slope2, masked, lim, n, lk);
+        float p[16], pd[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(x[r]);
+          if constexpr (DROP) {
+            const bool kp = kept(kw[r >> 2], r & 3, a.drop_t);
+            pd[r] = kp ? p[r] : 0.f;
+            p[r] = kp ? p[r] : -p[r];
+          } else {
+            pd[r] = p[r];
+          }
+        }
+        FA_LDS(f32x4_t)* px = pex + (j & 1) * kPB;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          px[g * 64] = f32x4_t{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+        frag pk[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+          u32x4_t up;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            up[e] = pack2(pd[8 * t + 2 * e], pd[8 * t + 2 * e + 1], (T*)nullptr);
+          pk[t] = __builtin_bit_cast(frag, up);
+        }
+        // dV^T += dO^T P
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mma(tr_frag<frag>(tdo, rl.trl[db], t, RB), pk[t], acc[db]);
+      }
+      step_end(c, j);
+    }
+  } else {
+    f32x16_t dpp = {};  // dP of the previous chunk
+    for (int c = c_begin; c <= nch; ++c) {
+      const int j = c - c_begin;
+      if (wave_live && c > c_begin && c - 1 >= c_wave) {
+        // chunk c - 1: dS = P o (dP - delta), dK^T += Q^T dS
+        const FA_LDS(char)* bp = smem + ((j + kStages - 1) % kStages) * kBufB;
+        const FA_LDS(float)* tlp = (const FA_LDS(float)*)(bp + 2 * TP::kTileB);
+        const FA_LDS(f32x4_t)* px = pex + ((j - 1) & 1) * kPB;
+        float ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_t p4 = px[g * 64];
+          const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tlp + kRows + 8 * g + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            if constexpr (DROP) {
+              const bool kp = !__builtin_signbit(p4[e]);
+              ds[r] = fabsf(p4[e]) * ((kp ? dpp[r] * a.drop_scale : 0.f) - d4[e]);
+            } else {
+              ds[r] = p4[e] * (dpp[r] - d4[e]);
+            }
+          }
+        }
+        frag pk[TS];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+          u32x4_t ud;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ud[e] = pack2(ds[8 * t + 2 * e], ds[8 * t + 2 * e + 1], (T*)nullptr);
+          pk[t] = __builtin_bit_cast(frag, ud);
+        }
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mma(tr_frag<frag>(bp, rl.trl[db], t, RB), pk[t], acc[db]);
+      }
+      if (wave_live && c < nch && c >= c_wave) {
+        // chunk c: dP = dO V^T
+        const FA_LDS(char)* tdo = smem + (j % kStages) * kBufB + TP::kTileB;
+        dpp = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dpp = mma(row_frag<frag>(tdo, rl.rowl[ks]), kv[ks], dpp);
+      }
+      step_end(c, j);
+    }
+  }
+
+  // dV = dV^T (times 1 / (1 - p) with dropout), dK = scale * dK^T, for keys
+  // < Nk (padding keys: zero)
+  const float sc = pw ? (DROP ? a.drop_scale : 1.f) : a.scale;
+  if (n < wi.kwrite) {
+    T* dst = (T*)(pw ? a.dv : a.dk) + ((size_t)wi.k_tok0 + n) * rs + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * hh;
+        const f32x16_t& aa = acc[db];
+        u32x2_t w = {pack2(aa[4 * g4] * sc, aa[4 * g4 + 1] * sc, (T*)nullptr),
+                     pack2(aa[4 * g4 + 2] * sc, aa[4 * g4 + 3] * sc, (T*)nullptr)};
+        *(u32x2_t*)(dst + d) = w;
       }
   }
 }
@@ -632,15 +925,29 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned nbh = (unsigned)(a.B * a.H);
+  static_assert(kKB == kNW, "both dK/dV kernels cover 128 keys per workgroup");
   const unsigned gk = (unsigned)((a.Nk + kNW * kRows - 1) / (kNW * kRows)) * nbh;
+  // head_dim 128: key blocks split over wave pairs (accumulators fit the VGPRs)
+#ifndef FA_BWD_SPLIT64
+#define FA_BWD_SPLIT64 0
+#endif
+#ifndef FA_BWD_SPLIT128
+#define FA_BWD_SPLIT128 1
+#endif
+  constexpr bool kSplit = D == 128 ? FA_BWD_SPLIT128 : FA_BWD_SPLIT64;
   const unsigned gq = (unsigned)a.nqb * nbh;
   const int mode = a.drop_t ? kBwdDrop : (a.alibi ? kBwdAlibi : kBwdPlain);
   auto launch2 = [&](auto mc, auto vc) {
     constexpr int M = decltype(mc)::value;
     constexpr bool V = decltype(vc)::value;
     if (gk > 0) {
-      if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, M, V>), dim3(gk), dim3(kNW * 64), 0, stream, a);
-      else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, M, V>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      if constexpr (kSplit) {
+        if (causal) hipLaunchKernelGGL((bwd_dkdv_split_kernel<T, D, true, M, V>), dim3(gk), dim3(kSplitNW * 64), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkdv_split_kernel<T, D, false, M, V>), dim3(gk), dim3(kSplitNW * 64), 0, stream, a);
+      } else {
+        if (causal) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, M, V>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+        else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, M, V>), dim3(gk), dim3(kNW * 64), 0, stream, a);
+      }
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
     }
