@@ -587,8 +587,8 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
       }
     }
   };
-  auto stage_store = [&](int buf) {
-    FA_LDS(char)* base = smem + buf * kBufB;
+  auto stage_store_at = [&](int off) {
+    FA_LDS(char)* base = smem + off;
     st.store(base, base + TP::kTileB, tid);
     if (tid < 2 * kRows) *(FA_LDS(float)*)(base + 2 * TP::kTileB + tid * 4) = st_l;
   };
@@ -600,22 +600,25 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
   // (c - c_begin) % 3, P of chunk c in half (c - c_begin) & 1.
   if (c_begin < nch) {
     stage_load(c_begin);
-    stage_store(0);
+    stage_store_at(0);
   }
   __syncthreads();
   if (c_begin + 1 < nch) stage_load(c_begin + 1);
-  // end of step c: stage chunk c + 1 (its stage's last readers ran in step
-  // c - 1), barrier, start loading chunk c + 2
-  auto step_end = [&](int c, int j) {
-    if (c + 1 < nch) stage_store((j + 1) % kStages);
+  // end of step c: stage chunk c + 1 at byte offset sn (that stage's last
+  // readers ran in step c - 1), barrier, start loading chunk c + 2
+  auto step_end = [&](int c, int sn) {
+    if (c + 1 < nch) stage_store_at(sn);
     __syncthreads();
     if (c + 2 < nch) stage_load(c + 2);
   };
+  // byte offset of the stage after the one at byte offset sc
+  auto next_stage = [](int sc) { return sc == (kStages - 1) * kBufB ? 0 : sc + kBufB; };
   // the two kinds of wave run separate loops with the same barriers
   if (pw) {
+    int sc = 0, ph = 0;  // stage (bytes) and P half (elements) of chunk c
     for (int c = c_begin; c <= nch; ++c) {
-      const int j = c - c_begin;
-      const FA_LDS(char)* base = smem + (j % kStages) * kBufB;
+      const int sn = next_stage(sc);
+      const FA_LDS(char)* base = smem + sc;
       const FA_LDS(char)* tq = base;
       const FA_LDS(char)* tdo = base + TP::kTileB;
       const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * TP::kTileB);
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
             pd[r] = p[r];
           }
         }
-        FA_LDS(f32x4_t)* px = pex + (j & 1) * kPB;
+        FA_LDS(f32x4_t)* px = pex + ph;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           px[g * 64] = f32x4_t{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
@@ -670,17 +673,21 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
           for (int db = 0; db < DB; ++db)
             acc[db] = mma(tr_frag<frag>(tdo, rl.trl[db], t, RB), pk[t], acc[db]);
       }
-      step_end(c, j);
+      step_end(c, sn);
+      sc = sn;
+      ph ^= kPB;
     }
   } else {
     f32x16_t dpp = {};  // dP of the previous chunk
+    // stages (bytes) of chunks c - 1 and c, P half (elements) of chunk c - 1
+    int sp = (kStages - 1) * kBufB, sc = 0, ph = kPB;
     for (int c = c_begin; c <= nch; ++c) {
-      const int j = c - c_begin;
+      const int sn = next_stage(sc);
       if (wave_live && c > c_begin && c - 1 >= c_wave) {
         // chunk c - 1: dS = P o (dP - delta), dK^T += Q^T dS
-        const FA_LDS(char)* bp = smem + ((j + kStages - 1) % kStages) * kBufB;
+        const FA_LDS(char)* bp = smem + sp;
         const FA_LDS(float)* tlp = (const FA_LDS(float)*)(bp + 2 * TP::kTileB);
-        const FA_LDS(f32x4_t)* px = pex + ((j - 1) & 1) * kPB;
+        const FA_LDS(f32x4_t)* px = pex + ph;
         float ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -714,12 +721,15 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
       }
       if (wave_live && c < nch && c >= c_wave) {
         // chunk c: dP = dO V^T
-        const FA_LDS(char)* tdo = smem + (j % kStages) * kBufB + TP::kTileB;
+        const FA_LDS(char)* tdo = smem + sc + TP::kTileB;
         dpp = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) dpp = mma(row_frag<frag>(tdo, rl.rowl[ks]), kv[ks], dpp);
       }
-      step_end(c, j);
+      step_end(c, sn);
+      sp = sc;
+      sc = sn;
+      ph ^= kPB;
     }
   }
 
