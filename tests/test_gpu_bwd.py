@@ -90,6 +90,14 @@ BWD = [
     (P("f16 D64 causal B2 H2 N300 padded keys", "f16", 64, True, 2, 2, 300, 300, 57), [300, 177]),
     (P("bf16 D128 noncausal B1 H1 Nq1 Nk1", "bf16", 128, False, 1, 1, 1, 1, 58), None),
     (P("f16 D64 causal B1 H4 N1000", "f16", 64, True, 1, 4, 1000, 1000, 59), None),
+    # head_dim 128 runs the two-wave dK/dV kernel: ragged causal shapes, and padded keys that
+    # leave whole 128-key workgroups past the sequence (no chunk to visit, zero rows to write)
+    (P("bf16 D128 causal Nq100 Nk300", "bf16", 128, True, 1, 2, 100, 300, 151), None),
+    (P("f16 D128 causal Nq300 Nk100 (rows with no visible key)", "f16", 128, True, 1, 2, 300, 100,
+       152), None),
+    (P("bf16 D128 causal B2 H2 N300 padded keys", "bf16", 128, True, 2, 2, 300, 300, 153), [300, 40]),
+    (P("f16 D128 noncausal B2 H1 Nq70 Nk390 padded keys", "f16", 128, False, 2, 1, 70, 390, 154),
+     [390, 129]),
 ]
 
 
@@ -148,6 +156,9 @@ MASKED_BWD = [
     (P("f16 D128 causal N257 prefix+ALiBi", "f16", 128, True, 1, 2, 257, 257, 66), 64, True, None),
     (P("f16 D64 causal B2 H2 N300 padded, prefix", "f16", 64, True, 2, 2, 300, 300, 67), 200,
      False, [300, 177]),
+    (P("bf16 D128 causal B2 H2 N300 padded, prefix", "bf16", 128, True, 2, 2, 300, 300, 68), 200,
+     False, [300, 177]),
+    (P("bf16 D128 causal Nq300 Nk100 ALiBi", "bf16", 128, True, 1, 3, 300, 100, 69), 0, True, None),
 ]
 
 
@@ -199,6 +210,8 @@ VARLEN_BWD = [
     ("bf16 D64 bidirectional H2 Lq != Lk", "bf16", 64, 2, False, [64, 200, 5], [190, 7, 128], 73),
     ("f16 D64 causal H4 8 short seqs", "f16", 64, 4, True, [17, 31, 32, 33, 63, 64, 65, 2],
      [17, 31, 32, 33, 63, 64, 65, 2], 74),
+    ("bf16 D128 causal H2 Lq != Lk", "bf16", 128, 2, True, [100, 260, 33], [300, 130, 33], 75),
+    ("f16 D128 bidirectional H2 Lq != Lk", "f16", 128, 2, False, [64, 200, 5], [190, 7, 128], 76),
 ]
 
 

@@ -81,6 +81,8 @@ FWD = [
     (W("bf16 D128 noncausal B2 H2 N160", "bf16", 128, False, 2, 2, 160, 160, 84), None, 0.9),
     (W("bf16 D64 causal Nq300 Nk100", "bf16", 64, True, 1, 2, 300, 100, 85), None, 0.3),
     (W("f16 D64 causal B2 H2 N300 padded keys", "f16", 64, True, 2, 2, 300, 300, 86), [300, 177], 0.2),
+    (W("bf16 D128 causal Nq300 Nk100", "bf16", 128, True, 1, 2, 300, 100, 87), None, 0.3),
+    (W("f16 D128 causal B2 H2 N300 padded keys", "f16", 128, True, 2, 2, 300, 300, 89), [300, 40], 0.2),
 ]
 
 
