@@ -890,6 +890,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     // pair p: exp2 in chunk p*RP, add and pack in chunk p*RP + ALAG; the
     // probabilities of block u-1 in pk[t] are read by the P V MFMAs of
     // chunks t*DB .. t*DB+DB-1, never after their replacement is written
+    // At head_dim 128 (MFMA-bound, two waves per SIMD) the chunks run at a
+    // raised wave priority: while one wave is in its MFMA chunks and the
+    // other in its exponent or row-sum work, the arbiter then issues the
+    // MFMAs first and the other wave's VALU work fills their cycles.  At
+    // head_dim 64 (VALU-bound, four waves) it measured no different.
+    constexpr bool kPrio = D == 128;
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < LA; ++i) read(i);
 #pragma unroll
@@ -900,6 +907,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
       if (c >= ALAG && (c - ALAG) % RP == 0) acc2((c - ALAG) / RP);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int p = 0; p < 8; ++p)
       if (p * RP + ALAG >= NCH) acc2(p);
