@@ -56,10 +56,13 @@ namespace fa {
 // exp2 units) raises the offset once the lazy check has fired.
 constexpr float kTau = 8.0f;
 
-template <typename T, int D, int QB, int KB, int NW, int NBUF>
+template <typename T, int D, int QB, int KB, int NW, int NBUF, bool KSPLIT = false>
 struct FwdCfg {
   static constexpr int kQW = 32 * QB;          // query rows per wave
-  static constexpr int kBR = NW * kQW;         // query rows per workgroup
+  // query rows per workgroup: with KSPLIT all waves share one row block and
+  // wave w takes 32-key block w of every tile (KB == NW)
+  static constexpr int kBR = KSPLIT ? kQW : NW * kQW;
+  static_assert(!KSPLIT || KB == NW, "one key block of each tile per wave");
   static constexpr int kBC = 32 * KB;          // keys per tile
   static constexpr int kNT = NW * 64;          // threads per workgroup
   static constexpr int kES = Elem<T>::kBytes;
@@ -178,9 +181,10 @@ __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
   return true;
 }
 
-template <typename T, int D, int QB, int KB, int NW, int NBUF, int OCC, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int QB, int KB, int NW, int NBUF, int OCC, bool KSPLIT, bool CAUSAL,
+          bool VARLEN>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
-  using C = FwdCfg<T, D, QB, KB, NW, NBUF>;
+  using C = FwdCfg<T, D, QB, KB, NW, NBUF, KSPLIT>;
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr bool F32 = (E::kBytes == 4);
@@ -211,8 +215,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
     const int kmax = min(q0 + C::kBR, lq) - 1 + off;
     nkt = kmax < 0 ? 0 : min(nkt_all, kmax / C::kBC + 1);
   }
-  const int wq0 = q0 + wave * C::kQW;
+  const int wq0 = KSPLIT ? q0 : q0 + wave * C::kQW;
   const int wq_last = min(wq0 + C::kQW, lq) - 1;
+  // key blocks of a tile this wave computes: all KB, or (KSPLIT) block kbo
+  constexpr int KBW = KSPLIT ? 1 : KB;
+  const int kbo = KSPLIT ? wave : 0;
 
   const size_t rs = (size_t)a.H * D;  // elements between consecutive tokens
   const T* qp = (const T*)a.q + (size_t)q_tok0 * rs + (size_t)h * D;
@@ -313,11 +320,19 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       vlane[i] = rr * RB + ((ch ^ swz_f<C::kCPR, F32>(rr)) * 16) + (qq & 1) * 8;
     }
   }
+  // this wave's key block within the tile (KSPLIT): 32 rows further on; the
+  // swizzles depend on row bits below 5 only, so it is a plain offset
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) klane[ks] += kbo * 32 * RB;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) vlane[i] += kbo * 32 * RB;
 
-  f32x16_t sacc[KB][QB];      // scores of the tile being processed
+  f32x16_t sacc[KBW][QB];     // scores of the tile being processed
 
   auto active = [&](int j) -> bool {
-    return j >= 0 && j < nkt && wq_last >= wq0 && (!CAUSAL || j * C::kBC <= wq_last + off);
+    const int k0w = j * C::kBC + kbo * 32;  // first key of this wave's part of tile j
+    return j >= 0 && j < nkt && wq_last >= wq0 && k0w < lk &&
+           (!CAUSAL || k0w <= wq_last + off);
   };
 
   auto scores = [&](int j) {
@@ -326,13 +341,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       const char* kt = (const char*)smem + sb;
       // S^T = K Q^T for KB key blocks x QB query blocks
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
           const frag kf = *(const frag*)(kt + klane[ks] + kb * 32 * RB);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
@@ -343,14 +358,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   };
 
   auto softmax = [&](int j) {
-    const int k0 = j * C::kBC;
-    const bool need_mask = (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > wq0 + off);
+    const int k0 = j * C::kBC + kbo * 32;  // first key of this wave's part of the tile
+    constexpr int kSpan = 32 * KBW;
+    const bool need_mask = (k0 + kSpan > lk) || (CAUSAL && k0 + kSpan - 1 > wq0 + off);
     {  // x = c S - m
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float ms = mrow[qb] == -INFINITY ? 0.f : mrow[qb];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = __builtin_fmaf(sacc[kb][qb][r], a.c, -ms);
       }
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
         const int qi = wq0 + qb * 32 + col;
         const int last = CAUSAL ? min(qi + off, lk - 1) : lk - 1;  // last visible key
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
           const float lim = (float)(last - k0 - kb * 32 - 4 * hh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
     // precision), then that block's P V products.
     const int vt_off = (j % NBUF) * C::kStageB + C::kTileB;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
       frag pk[TS][QB];
       float tsum[QB];
       auto probs = [&]() {
@@ -437,7 +453,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
 #pragma unroll
-          for (int k2 = kb; k2 < KB; ++k2)
+          for (int k2 = kb; k2 < KBW; ++k2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[k2][qb][r] -= delta;
         }
@@ -497,6 +513,71 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
     }
   }
 
+  if constexpr (KSPLIT) {
+    // ---- merge of the waves' partial results for the shared row block ----
+    // Wave w holds (m_w, l_w, O_w) over its key blocks.  With M = max_w m_w
+    // the row's result is sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w (the
+    // pairwise merge of the online softmax, here over four partials, added
+    // in wave order).  The staging buffers are reused for the exchange.
+    static_assert(QB == 1 && NW == 4, "one row block; wave w finishes register group w");
+    constexpr int kXO = 2 * NW * 32;  // floats before the partial outputs
+    static_assert((kXO + NW * DB * 16 * 64) * 4 <= C::kLdsB, "exchange fits the staging buffers");
+    float* xm = (float*)smem;  // [NW][32] offsets m_w
+    float* xl = xm + NW * 32;  // [NW][32] sums l_w
+    float* xo = xm + kXO;      // [NW][DB][16][64] weighted O_w, lane-major
+    const float lt = half_sum(lrow[0]);
+    __syncthreads();  // every wave is done with the staging buffers
+    if (hh == 0) {
+      xm[wave * 32 + col] = mrow[0];
+      xl[wave * 32 + col] = lt;
+    }
+    __syncthreads();
+    float mw[NW];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = xm[w * 32 + col];
+      M = fmaxf(M, mw[w]);
+    }
+    float wt[NW];  // weights 2^(m_w - M); 0 for a wave that saw no key
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wt[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[((wave * DB + db) * 16 + r) * 64 + lane] = oacc[db][0][r] * wt[wave];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += wt[w] * xl[w * 32 + col];
+    __syncthreads();
+    const int qi = wq0 + col;
+    if (qi < lq) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      T* orow = (T*)a.o + (size_t)(q_tok0 + qi) * rs + (size_t)h * D;
+      const int g4 = wave;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float acc = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) acc += xo[((w * DB + db) * 16 + 4 * g4 + e) * 64 + lane];
+          x[e] = acc * inv;
+        }
+        const int d = 32 * db + 8 * g4 + 4 * hh;
+        if constexpr (F32) {
+          *(float4*)(orow + d) = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          u32x2_t u = {pack2(x[0], x[1], (T*)nullptr), pack2(x[2], x[3], (T*)nullptr)};
+          *(u32x2_t*)(orow + d) = u;
+        }
+      }
+      if (wave == 0 && hh == 0 && a.lse)
+        a.lse[lse_base + qi] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   // ---- epilogue: O = O / l, lse = m + log2 l (converted to natural log) ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -1065,17 +1146,21 @@ hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int 
 #ifndef FA_TILE_16_128
 #define FA_TILE_16_128 1, 2, 4, 2, 2
 #endif
-template <int QB_, int KB_, int NW_, int NBUF_, int OCC_>
+template <int QB_, int KB_, int NW_, int NBUF_, int OCC_, int KSPLIT_ = 0>
 struct TileCfg {
   static constexpr int QB = QB_, KB = KB_, NW = NW_, NBUF = NBUF_, OCC = OCC_;
+  static constexpr bool KSPLIT = KSPLIT_ != 0;
 };
 template <typename T, int D> struct Tile;
 template <> struct Tile<__bf16, 64> : TileCfg<FA_TILE_16_64> {};
 template <> struct Tile<_Float16, 64> : TileCfg<FA_TILE_16_64> {};
 template <> struct Tile<__bf16, 128> : TileCfg<FA_TILE_16_128> {};
 template <> struct Tile<_Float16, 128> : TileCfg<FA_TILE_16_128> {};
+// fp32 at head_dim 64: 32-row workgroups whose four waves split each
+// 128-key tile (the longest causal row block otherwise walks every key on
+// one wave: fp32 MFMAs are 16 times slower per flop than bf16 ones)
 #ifndef FA_TILE_32_64
-#define FA_TILE_32_64 1, 2, 4, 2, 2
+#define FA_TILE_32_64 1, 4, 4, 2, 2, 1
 #endif
 #ifndef FA_TILE_32_128
 #define FA_TILE_32_128 1, 1, 4, 2, 2
@@ -1133,16 +1218,19 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
   }
   using Tl = Tile<T, D>;
   constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;
-  constexpr int lds = FwdCfg<T, D, QB, KB, NW, NB>::kLdsB;
+  constexpr bool KSP = Tl::KSPLIT;
+  constexpr int lds = FwdCfg<T, D, QB, KB, NW, NB, KSP>::kLdsB;
   if (causal) {
-    if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, true, true>, grid, NW * 64, lds, stream, a);
-    return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, true, false>, grid, NW * 64, lds, stream, a);
+    if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, true, true>, grid, NW * 64, lds, stream, a);
+    return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, true, false>, grid, NW * 64, lds, stream, a);
   }
-  if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, false, true>, grid, NW * 64, lds, stream, a);
-  return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, false, false>, grid, NW * 64, lds, stream, a);
+  if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, false, true>, grid, NW * 64, lds, stream, a);
+  return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, false, false>, grid, NW * 64, lds, stream, a);
 }
 
-template <typename T, int D> static int rows_t() { return Tile<T, D>::NW * 32 * Tile<T, D>::QB; }
+template <typename T, int D> static int rows_t() {
+  return (Tile<T, D>::KSPLIT ? 1 : Tile<T, D>::NW) * 32 * Tile<T, D>::QB;
+}
 template <typename T, int D> static int keys_t() { return 32 * Tile<T, D>::KB; }
 
 int fwd_block_rows(fa_dtype_t dtype, int D) {

@@ -79,6 +79,12 @@ PREFILL = [
     P("f16 D128 noncausal B2 H2 N200", "f16", 128, False, 2, 2, 200, 200),
     P("f32 D128 causal B1 H2 N150", "f32", 128, True, 1, 2, 150, 150),
     P("f32 D64 noncausal B1 H2 Nq70 Nk33", "f32", 64, False, 1, 2, 70, 33),
+    # fp32 at head_dim 64 splits each 128-key tile over the four waves of a
+    # 32-row workgroup and merges their partial results: rows with no visible
+    # key, waves whose key block lies past the end, several tiles per row block
+    P("f32 D64 causal Nq300 Nk100 (empty rows)", "f32", 64, True, 1, 2, 300, 100),
+    P("f32 D64 causal B2 Nq100 Nk300", "f32", 64, True, 2, 2, 100, 300),
+    P("f32 D64 noncausal Nq33 Nk700", "f32", 64, False, 1, 3, 33, 700),
     P("bf16 D64 N1", "bf16", 64, True, 1, 1, 1, 1),
     P("bf16 D64 Nq1 Nk1000 noncausal", "bf16", 64, False, 2, 2, 1, 1000),
     P("bf16 D64 causal Nq1 Nk300 (bottom-right)", "bf16", 64, True, 1, 2, 1, 300),
