@@ -17,6 +17,9 @@ The printed JSON line carries:
 * cpu_baseline the float64 CPU oracle timed on a bounded sample of the same
             prefill workload (test infrastructure; reported, not a target).
 
+``--config N`` times one workload of the table alone instead (add
+``--cpu-baseline`` to time the oracle on a sample of that workload too).
+
 ``traffic`` comes from committed rocprofv3 counter summaries under
 ``profiles/`` and is reported only while the kernel source they were taken
 on is unchanged (a hash of the source files is stored with them).
@@ -122,6 +125,71 @@ def cpu_baseline(w, budget_s=20.0):
         "kind": "oracle",
         "sample": "%d of %d (batch, head) slices of %s, %.1f s of float64 numpy (BLAS "
                   "threads = cores; exp single-threaded)" % (done, len(pairs), w.name, dt),
+    }
+
+
+def cpu_baseline_config(w, budget_s=20.0):
+    """The oracle on a bounded sample of one table workload, in that
+    workload's unit: whole (batch, head) slices of a prefill, whole
+    (sequence, head) pairs of a packed batch, whole batch entries (all heads)
+    of a decode.  Input generation is outside the timed region."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    done, work, spent = 0, 0.0, 0.0
+    wall0 = time.perf_counter()  # input generation counts against 3x the budget
+    if w.kind == "prefill":
+        if w.backward or w.dropout or w.prefix or w.alibi:
+            return None
+        return cpu_baseline(w, budget_s)
+    if w.kind == "varlen":
+        q, k, v, cu = wl.varlen_inputs(w)
+        units = [(s, h) for s in range(len(cu) - 1) for h in range(w.H)]
+        for s, h in units:
+            a, b = int(cu[s]), int(cu[s + 1])
+            qs, ks, vs = (wl.to_f64(t[a:b, h:h + 1])[None] for t in (q, k, v))
+            t0 = time.perf_counter()
+            oracle.attention(qs, ks, vs, w.scale, w.causal)
+            spent += time.perf_counter() - t0
+            L = b - a
+            work += 4.0 * w.D * (L * (L + 1) // 2 if w.causal else L * L)
+            done += 1
+            if spent > budget_s or time.perf_counter() - wall0 > 3 * budget_s:
+                break
+        what = "(sequence, head) pairs"
+        value, unit = work / spent / 1e12, "TFLOP/s"
+    elif w.kind == "decode":
+        lens = w.lengths()
+        q = wl.to_f64(wl.decode_query(w))
+        units = list(range(w.B))
+        es = 2 if w.dtype in ("bf16", "f16") else 4
+        for b in units:
+            L = int(lens[b])
+            kc = wl.to_f64(wl.decode_cache_rows(w, 1, b, L))[None]
+            vc = wl.to_f64(wl.decode_cache_rows(w, 2, b, L))[None]
+            t0 = time.perf_counter()
+            oracle.decode(q[b:b + 1], kc, vc, np.array([L]), w.scale)
+            spent += time.perf_counter() - t0
+            work += 2.0 * L * w.H * w.D * es
+            done += 1
+            if spent > budget_s or time.perf_counter() - wall0 > 3 * budget_s:
+                break
+        what = "batch entries (all heads)"
+        value, unit = work / spent / 1e9, "GB/s"
+    else:
+        return None
+    return {
+        "value": value,
+        "unit": unit,
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d %s of %s, %.1f s of float64 numpy (BLAS threads = cores)"
+                  % (done, len(units), what, w.name, spent),
     }
 
 
@@ -233,10 +301,14 @@ def run_config(n, args, dev):
     # HBM-side bytes per call from a committed counter summary, where one
     # exists for this workload and the kernel sources are unchanged since
     traffic = counters({9: "fa_bwd_causal_bf16_b4h16n8192d64.counters.json"}.get(n, ""))
-    print(json.dumps({"config": w.name, "kind": w.kind, "dtype": w.dtype, "value": val, "unit": unit,
-                      "ms_per_call": ms, "ms_median": med, "ms_min": t[0], "steps": args.steps,
-                      "roofline": {"bound": bound, "achieved": val, "peak": peak, "unit": unit,
-                                   "frac": val / peak, "traffic": traffic}}), flush=True)
+    line = {"config": w.name, "kind": w.kind, "dtype": w.dtype, "value": val, "unit": unit,
+            "ms_per_call": ms, "ms_median": med, "ms_min": t[0], "steps": args.steps,
+            "roofline": {"bound": bound, "achieved": val, "peak": peak, "unit": unit,
+                         "frac": val / peak, "traffic": traffic}}
+    if args.cpu_baseline:
+        log("timing the CPU oracle on a sample of %s" % w.name)
+        line["cpu_baseline"] = cpu_baseline_config(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -245,6 +317,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline", action="store_true",
+                    help="with --config: also time the CPU oracle on a bounded sample of that "
+                         "workload (forward prefill, varlen and decode workloads)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
