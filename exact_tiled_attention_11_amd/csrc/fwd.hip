@@ -42,6 +42,10 @@
 //  * Causal tiles wholly above the diagonal are never loaded; a wave whose
 //    rows cannot see a tile skips its math; only diagonal and tail tiles
 //    evaluate the mask.  Causal query blocks are issued longest first.
+//  * fp32 inputs take the plain tiled kernel (fp32 MFMA, no pipelining); at
+//    head_dim 64 the four waves of a workgroup share 32 query rows, split
+//    every key tile between them and merge their partial (m, l, O) at the
+//    end, which shortens the serial chain of the longest causal row block.
 
 #include <math.h>
 
