@@ -879,11 +879,24 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
       }
       dsk[t] = __builtin_bit_cast(frag, ud);
     }
-    // dQ^T += K^T dS^T (keys as the contraction index)
+    // dQ^T += K^T dS^T (keys as the contraction index).  At head_dim 128 (two
+    // waves per SIMD) these MFMAs issue at a raised wave priority, so they
+    // start ahead of the other wave's vector work (+1.7 %; no change at 64).
+    constexpr bool kPrio = D == 128;
+    if constexpr (kPrio) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int t = 0; t < TS; ++t)
 #pragma unroll
       for (int db = 0; db < DB; ++db) dqa[db] = mma(tr_frag<frag>(tk, rl.trl[db], t, RB), dsk[t], dqa[db]);
+    if constexpr (kPrio) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   if (nkb > 0) {
