@@ -197,7 +197,7 @@ def attention_dropout(q, k, v, scale, causal, dropout_p, seed, seqlens_k=None, r
 
 
 def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, seed=0, prefix=0,
-                  alibi_slopes=None):
+                  alibi_slopes=None, b0=0):
     """Gradients of the forward definition: given dO = dL/dO, returns
     (dQ, dK, dV) in the BSHD layout, float64.
 
@@ -215,7 +215,8 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, see
     (rowsum(dO o O) still equals rowsum(P o dP)).
     ``prefix`` and ``alibi_slopes`` select the forward's prefix mask and
     ALiBi bias (``visible``, ``alibi_bias``): the bias does not depend on q or
-    k, so it changes P but not the form of dS.
+    k, so it changes P but not the form of dS.  ``b0`` is the dropout
+    counters' batch index of entry 0 (a packed sequence passes its index).
     """
     q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
     B, nq, H, D = q.shape
@@ -244,7 +245,7 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, see
             p = np.where(ell[:, None] > 0, e / np.where(ell > 0, ell, 1.0)[:, None], 0.0)
             if dropout_p:
                 t = _dropout.drop_threshold(dropout_p)
-                z = _dropout.keep_mask(seed, b, h, np.arange(nq), lk, t) * _dropout.keep_scale(t)
+                z = _dropout.keep_mask(seed, b0 + b, h, np.arange(nq), lk, t) * _dropout.keep_scale(t)
             else:
                 z = np.ones_like(p)
             o = (p * z) @ vv
@@ -257,19 +258,25 @@ def attention_bwd(q, k, v, do, scale, causal, seqlens_k=None, dropout_p=0.0, see
     return dq, dk, dv
 
 
-def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, row_chunk=1024):
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, row_chunk=1024,
+                     prefix=0, alibi_slopes=None, dropout_p=0.0, seed=0):
     """Packed variable-length attention (the guide's flash_attn_varlen, FAQ 4).
 
     q: [total_q, H, D]; k, v: [total_k, H, D]; sequence s owns rows
     cu_seqlens_q[s]:cu_seqlens_q[s+1] of q and cu_seqlens_k[s]:cu_seqlens_k[s+1]
-    of k and v.  Each sequence attends only to its own keys.
-    Returns O [total_q, H, D] and lse [H, total_q].
+    of k and v.  Each sequence attends only to its own keys, with positions
+    counted within the sequence (so ``prefix``, the ALiBi distances and the
+    causal alignment are per sequence).  With ``dropout_p`` the keep decisions
+    are those of ``attention_dropout`` with the sequence index s in the
+    place of the batch index.
+    Returns O [total_q, H, D] and lse [H, total_q] (undropped).
     """
     q = np.asarray(q)
     total_q, H, D = q.shape
     o = np.zeros((total_q, H, v.shape[-1]), _F64)
     lse = np.zeros((H, total_q), _F64)
     nseq = len(cu_seqlens_q) - 1
+    t = _dropout.drop_threshold(dropout_p) if dropout_p else 0
     for s in range(nseq):
         q0, q1 = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
         k0, k1 = int(cu_seqlens_k[s]), int(cu_seqlens_k[s + 1])
@@ -278,17 +285,24 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, row_chu
             kb, vb = k[k0:k1, h, :], v[k0:k1, h, :]
             for r0 in range(0, lq, row_chunk):
                 r1 = min(lq, r0 + row_chunk)
-                ob, lb = attention_rows(q[q0 + r0:q0 + r1, h, :], np.arange(r0, r1), kb, vb,
-                                        lq, lk, scale, causal)
+                rows = np.arange(r0, r1)
+                keep = _dropout.keep_mask(seed, s, h, rows, lk, t) if dropout_p else None
+                ob, lb = attention_rows(q[q0 + r0:q0 + r1, h, :], rows, kb, vb, lq, lk, scale,
+                                        causal, prefix,
+                                        None if alibi_slopes is None else alibi_slopes[h],
+                                        keep=keep,
+                                        keep_scale=_dropout.keep_scale(t) if dropout_p else 1.0)
                 o[q0 + r0:q0 + r1, h, :] = ob
                 lse[h, q0 + r0:q0 + r1] = lb
     return o, lse
 
 
-def attention_varlen_bwd(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale, causal):
+def attention_varlen_bwd(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale, causal, prefix=0,
+                         alibi_slopes=None, dropout_p=0.0, seed=0):
     """Gradients of ``attention_varlen``: each packed sequence is its own
     attention problem, so its rows of (dQ, dK, dV) are ``attention_bwd`` of
-    that sequence alone.  q, do: [total_q, H, D]; k, v: [total_k, H, D].
+    that sequence alone (with its index as the dropout counters' batch
+    index).  q, do: [total_q, H, D]; k, v: [total_k, H, D].
     Keys outside every sequence get zero gradients.
     """
     q, k, v, do = (np.asarray(t) for t in (q, k, v, do))
@@ -299,7 +313,8 @@ def attention_varlen_bwd(q, k, v, do, cu_seqlens_q, cu_seqlens_k, scale, causal)
         q0, q1 = int(cu_seqlens_q[s]), int(cu_seqlens_q[s + 1])
         k0, k1 = int(cu_seqlens_k[s]), int(cu_seqlens_k[s + 1])
         gq, gk, gv = attention_bwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], do[None, q0:q1],
-                                   scale, causal)
+                                   scale, causal, dropout_p=dropout_p, seed=seed, prefix=prefix,
+                                   alibi_slopes=alibi_slopes, b0=s)
         dq[q0:q1], dk[k0:k1], dv[k0:k1] = gq[0], gk[0], gv[0]
     return dq, dk, dv
 
