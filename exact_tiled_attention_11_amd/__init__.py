@@ -27,7 +27,8 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FaError", "library_path", "load",
     "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_masked", "fa_bwd_dropout",
-    "fa_bwd_varlen",
+    "fa_bwd_varlen", "fa_fwd_varlen_masked", "fa_fwd_varlen_dropout", "fa_bwd_varlen_masked",
+    "fa_bwd_varlen_dropout",
     "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
     "fwd", "fwd_masked", "fwd_dropout", "bwd", "fwd_varlen", "bwd_varlen", "decode_splitkv",
@@ -54,6 +55,14 @@ _SIGS = {
                            _i, _vp, _i, _vp, _vp, _sz, _i, _vp]),
     "fa_bwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                            _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]),
+    "fa_fwd_varlen_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                  _i, _vp, _vp, _sz, _i, _vp]),
+    "fa_fwd_varlen_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                   _f, _u64, _vp, _sz, _i, _vp]),
+    "fa_bwd_varlen_masked": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                  _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _sz, _i, _vp]),
+    "fa_bwd_varlen_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                   _i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _vp, _sz, _i, _vp]),
@@ -139,6 +148,40 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
     return load().fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
                                 nseq, total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale,
                                 causal, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_fwd_varlen_masked(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                         D, scale, causal, prefix, alibi_slopes, workspace, workspace_bytes, dtype,
+                         stream) -> int:
+    return load().fa_fwd_varlen_masked(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
+                                       total_k, H, D, scale, causal, prefix, alibi_slopes,
+                                       workspace, workspace_bytes, dtype, stream)
+
+
+def fa_fwd_varlen_dropout(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                          D, scale, causal, dropout_p, seed, workspace, workspace_bytes, dtype,
+                          stream) -> int:
+    return load().fa_fwd_varlen_dropout(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq,
+                                        total_q, total_k, H, D, scale, causal, dropout_p, seed,
+                                        workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_varlen_masked(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal, prefix,
+                         alibi_slopes, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_varlen_masked(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q,
+                                       cu_seqlens_k, nseq, total_q, total_k, max_seqlen_q,
+                                       max_seqlen_k, H, D, scale, causal, prefix, alibi_slopes,
+                                       workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_varlen_dropout(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
+                          total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal,
+                          dropout_p, seed, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_varlen_dropout(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q,
+                                        cu_seqlens_k, nseq, total_q, total_k, max_seqlen_q,
+                                        max_seqlen_k, H, D, scale, causal, dropout_p, seed,
+                                        workspace, workspace_bytes, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, Nq) -> int:
@@ -338,9 +381,12 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] =
 
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
-               scale: Optional[float] = None, out=None, lse=None, return_lse: bool = True,
+               scale: Optional[float] = None, prefix: int = 0, alibi_slopes=None,
+               dropout_p: float = 0.0, seed: int = 0, out=None, lse=None, return_lse: bool = True,
                workspace=None, stream=None) -> Tuple:
-    """Packed varlen attention. q [total_q, H, D], k, v [total_k, H, D] -> (o, lse [H, total_q])."""
+    """Packed varlen attention. q [total_q, H, D], k, v [total_k, H, D] -> (o, lse [H, total_q]).
+    prefix / alibi_slopes (float32 [H] on the device) select fa_fwd_varlen_masked, dropout_p > 0
+    fa_fwd_varlen_dropout (positions and dropout counters per sequence)."""
     import torch
     total_q, H, D = q.shape
     total_k = k.shape[0]
@@ -356,19 +402,32 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
     need = fa_fwd_varlen_workspace_bytes(max(nseq, 1), total_q)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
-                       _ptr(cu_seqlens_k), nseq, total_q, total_k, H, D, float(scale),
-                       int(bool(causal)), _ptr(workspace), workspace.numel(), _dtype_code(q),
-                       _stream(stream))
-    _check("fa_fwd_varlen", st)
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H):
+        raise ValueError("alibi_slopes must be float32[H]")
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+              _ptr(cu_seqlens_k), nseq, total_q, total_k, H, D, float(scale), int(bool(causal)))
+    tail = (_ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
+    if dropout_p:
+        if prefix or alibi_slopes is not None:
+            raise ValueError("dropout does not combine with the prefix mask or ALiBi")
+        st = fa_fwd_varlen_dropout(*common, float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, *tail)
+        _check("fa_fwd_varlen_dropout", st)
+    elif prefix or alibi_slopes is not None:
+        st = fa_fwd_varlen_masked(*common, int(prefix), _ptr(alibi_slopes), *tail)
+        _check("fa_fwd_varlen_masked", st)
+    else:
+        st = fa_fwd_varlen(*common, *tail)
+        _check("fa_fwd_varlen", st)
     return out, lse
 
 
 def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
                scale: Optional[float] = None, max_seqlen_q: Optional[int] = None,
-               max_seqlen_k: Optional[int] = None, dq=None, dk=None, dv=None, workspace=None,
+               max_seqlen_k: Optional[int] = None, prefix: int = 0, alibi_slopes=None,
+               dropout_p: float = 0.0, seed: int = 0, dq=None, dk=None, dv=None, workspace=None,
                stream=None) -> Tuple:
-    """Gradients for fwd_varlen (packed q [total_q, H, D], k, v [total_k, H, D], lse [H, total_q]).
+    """Gradients for fwd_varlen (packed q [total_q, H, D], k, v [total_k, H, D], lse [H, total_q]),
+    with the forward call's prefix / alibi_slopes / dropout_p and seed.
     max_seqlen_q / max_seqlen_k default to the longest ranges of cu_seqlens (read on the host:
     pass them to avoid that synchronisation)."""
     import torch
@@ -389,12 +448,21 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: boo
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_bytes(1, H, total_q), 16), dtype=torch.uint8,
                                 device=q.device)
-    st = fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                       _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq, total_q,
-                       total_k, int(max_seqlen_q), int(max_seqlen_k), H, D, float(scale),
-                       int(bool(causal)), _ptr(workspace), workspace.numel(), _dtype_code(q),
-                       _stream(stream))
-    _check("fa_bwd_varlen", st)
+    common = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+              _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq, total_q, total_k,
+              int(max_seqlen_q), int(max_seqlen_k), H, D, float(scale), int(bool(causal)))
+    tail = (_ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
+    if dropout_p:
+        if prefix or alibi_slopes is not None:
+            raise ValueError("dropout does not combine with the prefix mask or ALiBi")
+        st = fa_bwd_varlen_dropout(*common, float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, *tail)
+        _check("fa_bwd_varlen_dropout", st)
+    elif prefix or alibi_slopes is not None:
+        st = fa_bwd_varlen_masked(*common, int(prefix), _ptr(alibi_slopes), *tail)
+        _check("fa_bwd_varlen_masked", st)
+    else:
+        st = fa_bwd_varlen(*common, *tail)
+        _check("fa_bwd_varlen", st)
     return dq, dk, dv
 
 

@@ -263,18 +263,26 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
 
 extern "C" {
 
-fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
-                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
-                          int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int H,
-                          int D, float scale, int causal, void* workspace, size_t workspace_bytes,
-                          fa_dtype_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status_t bwd_varlen_impl(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                            int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int H,
+                            int D, float scale, int causal, int prefix,
+                            const float* alibi_slopes, uint32_t drop_t, float drop_scale,
+                            uint64_t seed, void* workspace, size_t workspace_bytes,
+                            fa_dtype_t dtype, void* stream) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the backward kernels are 16-bit only
   if (nseq < 1 || H < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (prefix < 0 || (prefix > 0 && !causal)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)alibi_slopes & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (!cu_seqlens_q || !cu_seqlens_k || ((uintptr_t)cu_seqlens_q & 3u) != 0 ||
       ((uintptr_t)cu_seqlens_k & 3u) != 0)
     return FA_ERR_INVALID_ARG;
@@ -315,12 +323,62 @@ fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const voi
   a.nqb = (int)((max_seqlen_q + rows - 1) / rows);
   a.c = fmaxf(scale * kLog2eF, 1e-30f);
   a.scale = scale;
-  a.drop_scale = 1.f;
+  a.drop_t = drop_t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_scale = drop_scale;
+  a.prefix = prefix;
+  a.alibi = alibi_slopes;
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.total_q = total_q;
   a.total_k = total_k;
   return from_hip(fa::launch_bwd(a, dtype, D, causal != 0, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                          int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int H,
+                          int D, float scale, int causal, void* workspace, size_t workspace_bytes,
+                          fa_dtype_t dtype, void* stream) {
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal, 0,
+                         nullptr, 0u, 1.f, 0u, workspace, workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_bwd_varlen_masked(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk,
+                                 void* dv, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int nseq, int total_q, int total_k,
+                                 int max_seqlen_q, int max_seqlen_k, int H, int D, float scale,
+                                 int causal, int prefix, const float* alibi_slopes,
+                                 void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                                 void* stream) {
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal,
+                         prefix, alibi_slopes, 0u, 1.f, 0u, workspace, workspace_bytes, dtype,
+                         stream);
+}
+
+fa_status_t fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                  int total_k, int max_seqlen_q, int max_seqlen_k, int H, int D,
+                                  float scale, int causal, float dropout_p, uint64_t seed,
+                                  void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                                  void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal, 0,
+                         nullptr, t, sc, seed, workspace, workspace_bytes, dtype, stream);
 }
 
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
@@ -333,20 +391,29 @@ size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {
   return fa::varlen_sched_bytes(nseq, fa::varlen_max_tiles(nseq, total_q, rows));
 }
 
-fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
-                          int total_q, int total_k, int H, int D, float scale, int causal,
-                          void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Packed prefill with the optional mask families and dropout.
+fa_status_t fwd_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                            int total_q, int total_k, int H, int D, float scale, int causal,
+                            int prefix, const float* alibi_slopes, uint32_t drop_t,
+                            float drop_scale, uint64_t seed, void* workspace,
+                            size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
+  // the mask families and dropout are implemented by the 16-bit kernel only
+  if (dtype == FA_F32 && (prefix != 0 || alibi_slopes || drop_t)) return FA_ERR_UNSUPPORTED;
   if (nseq < 1 || H < 1 || total_q < 0 || total_k < 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (prefix < 0 || (prefix > 0 && !causal)) return FA_ERR_INVALID_ARG;
   if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
   if (total_q == 0) return FA_OK;
   if (!q || !o || ((!k || !v) && total_k > 0)) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(workspace))
+      !aligned16(workspace) || ((uintptr_t)alibi_slopes & 3u) != 0)
     return FA_ERR_INVALID_ARG;
   const int rows = fa::fwd_block_rows(dtype, D);
   const long long max_tiles = fa::varlen_max_tiles(nseq, total_q, rows);
@@ -375,7 +442,53 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   a.H = H;
   a.total_q = total_q;
   a.c = fmaxf(scale * kLog2eF, 1e-30f);  // a zero scale acts as a vanishing one
+  a.prefix = prefix;
+  a.alibi = alibi_slopes;
+  a.drop_t = drop_t;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.drop_scale = drop_scale;
   return from_hip(fa::launch_fwd(a, dtype, D, causal != 0, true, (unsigned)(max_tiles * H), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                          int total_q, int total_k, int H, int D, float scale, int causal,
+                          void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                          void* stream) {
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                         D, scale, causal, 0, nullptr, 0u, 1.f, 0u, workspace, workspace_bytes,
+                         dtype, stream);
+}
+
+fa_status_t fa_fwd_varlen_masked(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int nseq, int total_q, int total_k,
+                                 int H, int D, float scale, int causal, int prefix,
+                                 const float* alibi_slopes, void* workspace,
+                                 size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                         D, scale, causal, prefix, alibi_slopes, 0u, 1.f, 0u, workspace,
+                         workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                  int total_k, int H, int D, float scale, int causal,
+                                  float dropout_p, uint64_t seed, void* workspace,
+                                  size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;  // the dropout kernels are 16-bit only
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                         D, scale, causal, 0, nullptr, t, sc, seed, workspace, workspace_bytes,
+                         dtype, stream);
 }
 
 static bool chunk_ok(int chunk) { return chunk == 64 || chunk == 128 || chunk == 256 || chunk == 512; }

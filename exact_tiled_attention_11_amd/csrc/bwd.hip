@@ -981,8 +981,12 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
     return hipGetLastError();
   };
   using F = std::false_type;
-  // packed batches: plain mode only (the entry point checks)
-  if (varlen) return launch2(std::integral_constant<int, kBwdPlain>{}, std::true_type{});
+  using Tr = std::true_type;
+  if (varlen) {
+    if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{}, Tr{});
+    if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{}, Tr{});
+    return launch2(std::integral_constant<int, kBwdPlain>{}, Tr{});
+  }
   if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{}, F{});
   if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{}, F{});
   return launch2(std::integral_constant<int, kBwdPlain>{}, F{});

@@ -169,11 +169,11 @@ __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
     w.lse_base = ((long long)b * a.H + w.h) * a.Nq;
   } else {
     const int t = blockIdx.x / a.H;
-    w.b = 0;
     w.h = blockIdx.x - t * a.H;
     if (t >= a.sched[0]) return false;
     const int* tl = a.sched + 2 + 4 * a.nseq + 2 * t;
     const int s = tl[0];
+    w.b = s;  // the sequence takes the batch index's place (dropout counters)
     w.qblk = tl[1];
     const int* sq = a.sched + 2 + 4 * s;
     w.q_tok0 = sq[0];
@@ -664,8 +664,9 @@ struct PipeCfg {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-// MODE: kPipePlain, kPipeAlibi (ALiBi bias) or kPipeDrop (attention dropout);
-// the last two are fixed-length only.
+// MODE: kPipePlain, kPipeAlibi (ALiBi bias) or kPipeDrop (attention dropout),
+// fixed-length or packed (a packed sequence's index takes the batch index's
+// place in the dropout counters).
 constexpr int kPipePlain = 0, kPipeAlibi = 1, kPipeDrop = 2;
 
 template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN, int MODE>
@@ -1205,12 +1206,20 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
     constexpr int NW = 4, PK = D == 128 ? FA_PIPE_PK128 : FA_PIPE_PK64;
     constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
     constexpr int P0 = kPipePlain, PA = kPipeAlibi, PD = kPipeDrop;
-    if (a.alibi) {  // fixed-length only (the entry point checks)
-      if (causal) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PA>, grid, NW * 64, lds, stream, a);
+    if (a.alibi) {
+      if (causal) {
+        if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, PA>, grid, NW * 64, lds, stream, a);
+        return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PA>, grid, NW * 64, lds, stream, a);
+      }
+      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, PA>, grid, NW * 64, lds, stream, a);
       return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, PA>, grid, NW * 64, lds, stream, a);
     }
-    if (a.drop_t) {  // fixed-length only (the entry point checks)
-      if (causal) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PD>, grid, NW * 64, lds, stream, a);
+    if (a.drop_t) {
+      if (causal) {
+        if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, PD>, grid, NW * 64, lds, stream, a);
+        return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PD>, grid, NW * 64, lds, stream, a);
+      }
+      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, PD>, grid, NW * 64, lds, stream, a);
       return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, PD>, grid, NW * 64, lds, stream, a);
     }
     if (causal) {

@@ -268,6 +268,56 @@ FA355_API fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v
                                      uint64_t seed, void* workspace, size_t workspace_bytes,
                                      fa_dtype_t dtype, void* stream);
 
+/*
+ * Packed variable-length batches with the mask families or dropout: the
+ * options of fa_fwd_masked / fa_fwd_dropout (the guide's flash_attn_varlen
+ * parameter table names causal, alibi_slopes and dropout_p for the packed
+ * call too) on the batches of fa_fwd_varlen, and their gradients on those of
+ * fa_bwd_varlen.  Positions count within each sequence: query row i of
+ * sequence s sits at key position i + Lk(s) - Lq(s), the prefix covers
+ * that sequence's keys [0, prefix), ALiBi distances are within the
+ * sequence, and the dropout counters take the sequence index s in the
+ * place of the batch index b.  fp16/bf16 only (fp32: FA_ERR_UNSUPPORTED);
+ * ALiBi and dropout do not combine (there is no entry point for both).
+ * Arguments, layouts, workspaces, errors and ordering as fa_fwd_varlen /
+ * fa_bwd_varlen plus, for the options, as fa_fwd_masked / fa_fwd_dropout;
+ * a backward call must repeat the forward call's options.
+ */
+FA355_API fa_status_t fa_fwd_varlen_masked(const void* q, const void* k, const void* v, void* o,
+                                           float* lse, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                           int total_k, int H, int D, float scale, int causal,
+                                           int prefix, const float* alibi_slopes,
+                                           void* workspace, size_t workspace_bytes,
+                                           fa_dtype_t dtype, void* stream);
+FA355_API fa_status_t fa_fwd_varlen_dropout(const void* q, const void* k, const void* v, void* o,
+                                            float* lse, const int32_t* cu_seqlens_q,
+                                            const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                            int total_k, int H, int D, float scale, int causal,
+                                            float dropout_p, uint64_t seed, void* workspace,
+                                            size_t workspace_bytes, fa_dtype_t dtype,
+                                            void* stream);
+FA355_API fa_status_t fa_bwd_varlen_masked(const void* q, const void* k, const void* v,
+                                           const void* o, const float* lse, const void* dout,
+                                           void* dq, void* dk, void* dv,
+                                           const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                           int total_k, int max_seqlen_q, int max_seqlen_k,
+                                           int H, int D, float scale, int causal, int prefix,
+                                           const float* alibi_slopes, void* workspace,
+                                           size_t workspace_bytes, fa_dtype_t dtype,
+                                           void* stream);
+FA355_API fa_status_t fa_bwd_varlen_dropout(const void* q, const void* k, const void* v,
+                                            const void* o, const float* lse, const void* dout,
+                                            void* dq, void* dk, void* dv,
+                                            const int32_t* cu_seqlens_q,
+                                            const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                            int total_k, int max_seqlen_q, int max_seqlen_k,
+                                            int H, int D, float scale, int causal,
+                                            float dropout_p, uint64_t seed, void* workspace,
+                                            size_t workspace_bytes, fa_dtype_t dtype,
+                                            void* stream);
+
 /* Static strings; never NULL. */
 FA355_API const char* fa_status_string(fa_status_t status);
 FA355_API const char* fa_version(void);

@@ -26,9 +26,10 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert names == sorted([
-        "fa_bwd", "fa_bwd_dropout", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_workspace_bytes",
-        "fa_fwd_dropout",
-        "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes",
+        "fa_bwd", "fa_bwd_dropout", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_varlen_dropout",
+        "fa_bwd_varlen_masked", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
+        "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_dropout",
+        "fa_fwd_varlen_masked", "fa_fwd_varlen_workspace_bytes",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
         "fa_version"])
@@ -291,3 +292,69 @@ def test_bwd_varlen_validation():
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
     assert call(wsb=fa.fa_bwd_workspace_bytes(1, 2, 100) - 1) == fa.FA_ERR_WORKSPACE
     assert call(tq=0, tk=0) == fa.FA_OK
+
+
+def test_varlen_masked_and_dropout_validation():
+    """The packed entry points with the mask families or dropout check their
+    options before any HIP call, as the fixed-length ones do."""
+    fb = dict(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, nseq=2, tq=10, tk=10, H=2, D=128, scale=0.1,
+              causal=1, ws=P, wsb=1 << 20, dtype=fa.FA_F16, stream=None)
+
+    def fmask(prefix=4, alibi=P, **kw):
+        a = dict(fb)
+        a.update(kw)
+        return fa.fa_fwd_varlen_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                       a["nseq"], a["tq"], a["tk"], a["H"], a["D"], a["scale"],
+                                       a["causal"], prefix, alibi, a["ws"], a["wsb"], a["dtype"],
+                                       a["stream"])
+
+    def fdrop(p=0.1, seed=1, **kw):
+        a = dict(fb)
+        a.update(kw)
+        return fa.fa_fwd_varlen_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"],
+                                        a["ck"], a["nseq"], a["tq"], a["tk"], a["H"], a["D"],
+                                        a["scale"], a["causal"], p, seed, a["ws"], a["wsb"],
+                                        a["dtype"], a["stream"])
+    assert fmask(prefix=-1) == fa.FA_ERR_INVALID_ARG
+    assert fmask(causal=0) == fa.FA_ERR_INVALID_ARG           # a prefix needs the causal mask
+    assert fmask(alibi=P + 2) == fa.FA_ERR_INVALID_ARG        # slopes not 4-byte aligned
+    assert fmask(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert fmask(ws=None) == fa.FA_ERR_WORKSPACE
+    assert fmask(tq=0) == fa.FA_OK
+    assert fdrop(p=1.0) == fa.FA_ERR_INVALID_ARG
+    assert fdrop(p=-0.1) == fa.FA_ERR_INVALID_ARG
+    assert fdrop(p=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert fdrop(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert fdrop(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert fdrop(tq=0) == fa.FA_OK
+
+    bb = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, cq=P, ck=P, nseq=3, tq=100,
+              tk=120, mq=50, mk=60, H=2, D=64, scale=0.1, causal=1, ws=P, wsb=1 << 20,
+              dtype=fa.FA_BF16, stream=None)
+
+    def bargs(a):
+        return (a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                a["cq"], a["ck"], a["nseq"], a["tq"], a["tk"], a["mq"], a["mk"], a["H"], a["D"],
+                a["scale"], a["causal"])
+
+    def bmask(prefix=4, alibi=P, **kw):
+        a = dict(bb)
+        a.update(kw)
+        return fa.fa_bwd_varlen_masked(*bargs(a), prefix, alibi, a["ws"], a["wsb"], a["dtype"],
+                                       a["stream"])
+
+    def bdrop(p=0.1, seed=1, **kw):
+        a = dict(bb)
+        a.update(kw)
+        return fa.fa_bwd_varlen_dropout(*bargs(a), p, seed, a["ws"], a["wsb"], a["dtype"],
+                                        a["stream"])
+    assert bmask(prefix=-1) == fa.FA_ERR_INVALID_ARG
+    assert bmask(causal=0) == fa.FA_ERR_INVALID_ARG
+    assert bmask(alibi=P + 2) == fa.FA_ERR_INVALID_ARG
+    assert bmask(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bmask(wsb=8) == fa.FA_ERR_WORKSPACE
+    assert bmask(tq=0, tk=0) == fa.FA_OK
+    assert bdrop(p=1.5) == fa.FA_ERR_INVALID_ARG
+    assert bdrop(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bdrop(ws=None) == fa.FA_ERR_WORKSPACE
+    assert bdrop(tq=0, tk=0) == fa.FA_OK

@@ -1,0 +1,140 @@
+"""GPU parity of packed variable-length batches with the prefix mask, ALiBi
+and attention dropout (fa_fwd_varlen_masked / _dropout and fa_bwd_varlen_
+masked / _dropout through the C ABI) against the oracle's packed forms.
+
+* Outputs and log-sum-exp against ``oracle.attention_varlen`` with the same
+  options; gradients against ``oracle.attention_varlen_bwd``.  Ragged
+  lengths, an empty sequence, Lq != Lk, both head dims, both dtypes.
+* Packing: equal-length sequences packed end to end give the fixed-length
+  entry points' results bit for bit (same tiles, the sequence index in the
+  batch index's place in the dropout counters).
+* Every call runs twice and must be bit-identical.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import assert_close, assert_grad_close
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _fa():
+    import exact_tiled_attention_11_amd as fa
+    fa.load()
+    return fa
+
+
+def _inputs(name, dtype, D, H, lens_q, lens_k, seed):
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    w = wl.Workload(name, "varlen", dtype, H=H, D=D, causal=True, scale=1 / math.sqrt(D), seed=seed)
+    q = wl.tensor(w, 0, (int(cu_q[-1]), H, D))
+    k = wl.tensor(w, 1, (int(cu_k[-1]), H, D))
+    v = wl.tensor(w, 2, (int(cu_k[-1]), H, D))
+    do = wl.tensor(w, 3, (int(cu_q[-1]), H, D))
+    return w, q, k, v, do, cu_q, cu_k
+
+
+CASES = [
+    # name, dtype, D, H, causal, lens_q, lens_k, options
+    ("bf16 D64 causal prefix 40", "bf16", 64, 3, True, [100, 260, 33, 0], [100, 260, 33, 0],
+     dict(prefix=40)),
+    ("f16 D128 causal ALiBi Lq != Lk", "f16", 128, 2, True, [100, 260, 33], [300, 130, 33],
+     dict(alibi=True)),
+    ("bf16 D64 bidirectional ALiBi", "bf16", 64, 4, False, [64, 200, 5], [190, 7, 128],
+     dict(alibi=True)),
+    ("bf16 D128 causal prefix+ALiBi", "bf16", 128, 2, True, [300, 129, 1], [300, 129, 1],
+     dict(prefix=100, alibi=True)),
+    ("f16 D64 causal dropout 0.2", "f16", 64, 3, True, [100, 260, 0, 33], [100, 260, 0, 33],
+     dict(dropout=0.2)),
+    ("bf16 D128 causal dropout 0.3 Lq != Lk", "bf16", 128, 2, True, [100, 260, 33],
+     [300, 130, 33], dict(dropout=0.3)),
+    ("bf16 D64 bidirectional dropout 0.5", "bf16", 64, 2, False, [64, 200, 5], [190, 7, 128],
+     dict(dropout=0.5)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_forward_and_gradients(case):
+    name, dtype, D, H, causal, lens_q, lens_k, opt = case
+    fa = _fa()
+    w, q, k, v, do, cu_q, cu_k = _inputs(name, dtype, D, H, lens_q, lens_k, 500 + len(name))
+    slopes = wl.alibi_slopes(H) if opt.get("alibi") else None
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+    prefix = opt.get("prefix", 0)
+    p = float(np.float32(opt.get("dropout", 0.0)))
+    seed = 7000 + len(name)
+    kw = dict(prefix=prefix, alibi_slopes=sd, dropout_p=p, seed=seed)
+    cqd, ckd = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    mq, mk = int(max(lens_q)), int(max(lens_k))
+    outs = []
+    for rep in range(2):
+        say("  varlen %s rep %d" % (name, rep))
+        o = torch.full_like(qd, float("nan"))
+        lse = torch.full((H, qd.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+        fa.fwd_varlen(qd, kd, vd, cqd, ckd, causal=causal, scale=w.scale, out=o, lse=lse, **kw)
+        dq = torch.full_like(qd, float("nan"))
+        dk = torch.full_like(kd, float("nan"))
+        dv = torch.full_like(vd, float("nan"))
+        fa.bwd_varlen(qd, kd, vd, o, lse, dod, cqd, ckd, causal=causal, scale=w.scale,
+                      max_seqlen_q=mq, max_seqlen_k=mk, dq=dq, dk=dk, dv=dv, **kw)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (o, lse, dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "run-to-run difference"
+    o, lse, dq, dk, dv = outs[0]
+    okw = dict(prefix=prefix, alibi_slopes=slopes, dropout_p=p, seed=seed)
+    o_ref, lse_ref = oracle.attention_varlen(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), cu_q, cu_k,
+                                             w.scale, causal, **okw)
+    ks = oracle.keep_scale(oracle.drop_threshold(p)) if p else 1.0
+    assert_close(dtype, wl.to_f64(o) / ks, o_ref / ks, lse.double().numpy(), lse_ref, name)
+    rq, rk, rv = oracle.attention_varlen_bwd(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v),
+                                             wl.to_f64(do), cu_q, cu_k, w.scale, causal, **okw)
+    assert_grad_close(dtype, wl.to_f64(dq), rq, "%s dq" % name)
+    assert_grad_close(dtype, wl.to_f64(dk), rk, "%s dk" % name)
+    assert_grad_close(dtype, wl.to_f64(dv), rv, "%s dv" % name)
+
+
+@pytest.mark.parametrize("opt", [dict(prefix=50), dict(alibi=True), dict(dropout=0.25)],
+                         ids=["prefix", "alibi", "dropout"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_equal_lengths_match_the_fixed_length_entry_points(opt, D):
+    fa = _fa()
+    B, L, H = 3, 300, 2
+    w = wl.Workload("pack", "prefill", "bf16", H=H, D=D, causal=True, scale=1 / math.sqrt(D),
+                    seed=900 + D, B=B, Nq=L, Nk=L)
+    q, k, v = (t.cuda() for t in wl.prefill_inputs(w))
+    do = wl.tensor(w, 3, (B, L, H, D)).cuda()
+    sd = torch.from_numpy(wl.alibi_slopes(H)).cuda() if opt.get("alibi") else None
+    p = float(np.float32(opt.get("dropout", 0.0)))
+    prefix = opt.get("prefix", 0)
+    say("  packing %s D%d" % (sorted(opt), D))
+    if p:
+        of, lf = fa.fwd_dropout(q, k, v, dropout_p=p, seed=77, causal=True, scale=w.scale)
+    else:
+        of, lf = fa.fwd_masked(q, k, v, causal=True, scale=w.scale, prefix=prefix, alibi_slopes=sd)
+    gf = fa.bwd(q, k, v, of, lf, do, causal=True, scale=w.scale, prefix=prefix, alibi_slopes=sd,
+                dropout_p=p, seed=77)
+    cu = torch.arange(B + 1, dtype=torch.int32, device="cuda") * L
+    pk = lambda t: t.reshape(B * L, H, D)
+    ov, lv = fa.fwd_varlen(pk(q), pk(k), pk(v), cu, cu, causal=True, scale=w.scale, prefix=prefix,
+                           alibi_slopes=sd, dropout_p=p, seed=77)
+    gv = fa.bwd_varlen(pk(q), pk(k), pk(v), ov, lv, pk(do), cu, cu, causal=True, scale=w.scale,
+                       prefix=prefix, alibi_slopes=sd, dropout_p=p, seed=77)
+    torch.cuda.synchronize()
+    assert torch.equal(pk(of).view(torch.int16), ov.view(torch.int16))
+    assert torch.equal(lf.permute(1, 0, 2).reshape(H, B * L).contiguous().view(torch.int32),
+                       lv.view(torch.int32))
+    for a, b in zip(gf, gv):
+        assert torch.equal(pk(a).view(torch.int16), b.view(torch.int16))
