@@ -28,10 +28,10 @@ __all__ = [
     "FaError", "library_path", "load",
     "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_masked", "fa_bwd_dropout",
     "fa_bwd_varlen", "fa_fwd_varlen_masked", "fa_fwd_varlen_dropout", "fa_bwd_varlen_masked",
-    "fa_bwd_varlen_dropout",
+    "fa_bwd_varlen_dropout", "fa_fwd_ex", "fa_bwd_ex", "fa_fwd_varlen_ex", "fa_bwd_varlen_ex",
     "fa_bwd_workspace_bytes", "fa_fwd_varlen", "fa_fwd_varlen_workspace_bytes", "fa_decode_splitkv",
     "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string", "fa_version",
-    "fwd", "fwd_masked", "fwd_dropout", "bwd", "fwd_varlen", "bwd_varlen", "decode_splitkv",
+    "fwd", "fwd_masked", "fwd_dropout", "fwd_ex", "bwd", "fwd_varlen", "bwd_varlen", "decode_splitkv",
     "decode_splitkv_paged",
 ]
 
@@ -63,6 +63,14 @@ _SIGS = {
                                   _i, _i, _i, _i, _i, _f, _i, _i, _vp, _vp, _sz, _i, _vp]),
     "fa_bwd_varlen_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                    _i, _i, _i, _i, _i, _f, _i, _f, _u64, _vp, _sz, _i, _vp]),
+    "fa_fwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _f,
+                       _u64, _i, _vp]),
+    "fa_bwd_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                       _vp, _i, _vp, _f, _u64, _vp, _sz, _i, _vp]),
+    "fa_fwd_varlen_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
+                              _vp, _f, _u64, _vp, _sz, _i, _vp]),
+    "fa_bwd_varlen_ex": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                              _i, _i, _i, _i, _f, _i, _i, _vp, _f, _u64, _vp, _sz, _i, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _vp, _sz, _i, _vp]),
@@ -182,6 +190,37 @@ def fa_bwd_varlen_dropout(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_se
                                         cu_seqlens_k, nseq, total_q, total_k, max_seqlen_q,
                                         max_seqlen_k, H, D, scale, causal, dropout_p, seed,
                                         workspace, workspace_bytes, dtype, stream)
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix, alibi_slopes,
+              dropout_p, seed, dtype, stream) -> int:
+    return load().fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
+                            alibi_slopes, dropout_p, seed, dtype, stream)
+
+
+def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
+              alibi_slopes, dropout_p, seed, workspace, workspace_bytes, dtype, stream) -> int:
+    return load().fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal,
+                            seqlens_k, prefix, alibi_slopes, dropout_p, seed, workspace,
+                            workspace_bytes, dtype, stream)
+
+
+def fa_fwd_varlen_ex(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H, D,
+                     scale, causal, prefix, alibi_slopes, dropout_p, seed, workspace,
+                     workspace_bytes, dtype, stream) -> int:
+    return load().fa_fwd_varlen_ex(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
+                                   total_k, H, D, scale, causal, prefix, alibi_slopes, dropout_p,
+                                   seed, workspace, workspace_bytes, dtype, stream)
+
+
+def fa_bwd_varlen_ex(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
+                     total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal, prefix,
+                     alibi_slopes, dropout_p, seed, workspace, workspace_bytes, dtype,
+                     stream) -> int:
+    return load().fa_bwd_varlen_ex(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k,
+                                   nseq, total_q, total_k, max_seqlen_q, max_seqlen_k, H, D,
+                                   scale, causal, prefix, alibi_slopes, dropout_p, seed,
+                                   workspace, workspace_bytes, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, Nq) -> int:
@@ -337,12 +376,40 @@ def fwd_dropout(q, k, v, *, dropout_p: float, seed: int, causal: bool = False,
     return out, lse
 
 
+def fwd_ex(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
+           prefix: int = 0, alibi_slopes=None, dropout_p: float = 0.0, seed: int = 0, out=None,
+           lse=None, return_lse: bool = True, stream=None) -> Tuple:
+    """fwd with every option at once: the prefix mask (causal only), ALiBi slopes (float32 [H]
+    on the device) and attention dropout (fp16/bf16 for any option)."""
+    import torch
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H):
+        raise ValueError("alibi_slopes must be float32[H]")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
+        raise ValueError("seqlens_k must be int32[B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D, float(scale),
+                   int(bool(causal)), _ptr(seqlens_k), int(prefix), _ptr(alibi_slopes),
+                   float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _dtype_code(q),
+                   _stream(stream))
+    _check("fa_fwd_ex", st)
+    return out, lse
+
+
 def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] = None,
         seqlens_k=None, dropout_p: float = 0.0, seed: int = 0, prefix: int = 0,
         alibi_slopes=None, dq=None, dk=None, dv=None, workspace=None, stream=None) -> Tuple:
     """Gradients (dq, dk, dv) for the forward fwd(q, k, v) that produced o and lse, given dout
     (with dropout_p > 0: for fwd_dropout with the same dropout_p and seed; with prefix or
-    alibi_slopes: for fwd_masked with the same ones)."""
+    alibi_slopes: for fwd_masked with the same ones; with both: for fwd_ex)."""
     import torch
     B, Nq, H, D = q.shape
     Nk = k.shape[1]
@@ -354,12 +421,18 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] =
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
                                 device=q.device)
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
+                                     alibi_slopes.numel() != H):
+        raise ValueError("alibi_slopes must be float32[H]")
     if dropout_p and (prefix or alibi_slopes is not None):
-        raise ValueError("dropout with the prefix mask or ALiBi has no backward")
+        st = fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                       _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                       _ptr(seqlens_k), int(prefix), _ptr(alibi_slopes), float(dropout_p),
+                       int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(workspace), workspace.numel(),
+                       _dtype_code(q), _stream(stream))
+        _check("fa_bwd_ex", st)
+        return dq, dk, dv
     if prefix or alibi_slopes is not None:
-        if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
-                                         alibi_slopes.numel() != H):
-            raise ValueError("alibi_slopes must be float32[H]")
         st = fa_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                            _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
                            _ptr(seqlens_k), int(prefix), _ptr(alibi_slopes), _ptr(workspace),
@@ -407,9 +480,11 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
               _ptr(cu_seqlens_k), nseq, total_q, total_k, H, D, float(scale), int(bool(causal)))
     tail = (_ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
-    if dropout_p:
-        if prefix or alibi_slopes is not None:
-            raise ValueError("dropout does not combine with the prefix mask or ALiBi")
+    if dropout_p and (prefix or alibi_slopes is not None):
+        st = fa_fwd_varlen_ex(*common, int(prefix), _ptr(alibi_slopes), float(dropout_p),
+                              int(seed) & 0xFFFFFFFFFFFFFFFF, *tail)
+        _check("fa_fwd_varlen_ex", st)
+    elif dropout_p:
         st = fa_fwd_varlen_dropout(*common, float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, *tail)
         _check("fa_fwd_varlen_dropout", st)
     elif prefix or alibi_slopes is not None:
@@ -452,9 +527,11 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: boo
               _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseq, total_q, total_k,
               int(max_seqlen_q), int(max_seqlen_k), H, D, float(scale), int(bool(causal)))
     tail = (_ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
-    if dropout_p:
-        if prefix or alibi_slopes is not None:
-            raise ValueError("dropout does not combine with the prefix mask or ALiBi")
+    if dropout_p and (prefix or alibi_slopes is not None):
+        st = fa_bwd_varlen_ex(*common, int(prefix), _ptr(alibi_slopes), float(dropout_p),
+                              int(seed) & 0xFFFFFFFFFFFFFFFF, *tail)
+        _check("fa_bwd_varlen_ex", st)
+    elif dropout_p:
         st = fa_bwd_varlen_dropout(*common, float(dropout_p), int(seed) & 0xFFFFFFFFFFFFFFFF, *tail)
         _check("fa_bwd_varlen_dropout", st)
     elif prefix or alibi_slopes is not None:

@@ -114,6 +114,12 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
                      int D, float scale, int causal, const int32_t* seqlens_k, int prefix,
                      const float* alibi_slopes, uint32_t drop_t, float drop_scale, uint64_t seed,
                      void* workspace, size_t workspace_bytes, fa_dtype_t dtype, void* stream);
+fa_status_t fwd_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                            int total_q, int total_k, int H, int D, float scale, int causal,
+                            int prefix, const float* alibi_slopes, uint32_t drop_t,
+                            float drop_scale, uint64_t seed, void* workspace,
+                            size_t workspace_bytes, fa_dtype_t dtype, void* stream);
 
 }  // namespace
 
@@ -379,6 +385,61 @@ fa_status_t fa_bwd_varlen_dropout(const void* q, const void* k, const void* v, c
   return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
                          total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal, 0,
                          nullptr, t, sc, seed, workspace, workspace_bytes, dtype, stream);
+}
+
+// Every option at once (the mask families and dropout together).
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Nq, int Nk, int D, float scale, int causal,
+                      const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
+                      float dropout_p, uint64_t seed, fa_dtype_t dtype, void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return fwd_fixed(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, seqlens_k, prefix,
+                   alibi_slopes, t, sc, seed, dtype, stream);
+}
+
+fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int H, int Nq,
+                      int Nk, int D, float scale, int causal, const int32_t* seqlens_k,
+                      int prefix, const float* alibi_slopes, float dropout_p, uint64_t seed,
+                      void* workspace, size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, seqlens_k,
+                  prefix, alibi_slopes, t, sc, seed, workspace, workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_fwd_varlen_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                             int total_q, int total_k, int H, int D, float scale, int causal,
+                             int prefix, const float* alibi_slopes, float dropout_p,
+                             uint64_t seed, void* workspace, size_t workspace_bytes,
+                             fa_dtype_t dtype, void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                         D, scale, causal, prefix, alibi_slopes, t, sc, seed, workspace,
+                         workspace_bytes, dtype, stream);
+}
+
+fa_status_t fa_bwd_varlen_ex(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                             int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int H,
+                             int D, float scale, int causal, int prefix,
+                             const float* alibi_slopes, float dropout_p, uint64_t seed,
+                             void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                             void* stream) {
+  uint32_t t = 0;
+  float sc = 1.f;
+  if (!drop_threshold(dropout_p, t, sc)) return FA_ERR_INVALID_ARG;
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, nseq,
+                         total_q, total_k, max_seqlen_q, max_seqlen_k, H, D, scale, causal,
+                         prefix, alibi_slopes, t, sc, seed, workspace, workspace_bytes, dtype,
+                         stream);
 }
 
 size_t fa_fwd_varlen_workspace_bytes(int nseq, int total_q) {

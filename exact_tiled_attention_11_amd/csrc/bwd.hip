@@ -48,8 +48,8 @@ namespace {
 
 constexpr int kNW = 4;     // waves per workgroup
 
-// MODE of the gradient kernels: plain, with the ALiBi bias of the forward,
-// or with its attention dropout (the prefix mask is a runtime value in all)
+// MODE of the gradient kernels: bit flags for the ALiBi bias of the forward
+// and for its attention dropout (the prefix mask is a runtime value in all)
 constexpr int kBwdPlain = 0, kBwdAlibi = 1, kBwdDrop = 2;
 constexpr int kRows = 32;  // rows per wave and per streamed tile
 
@@ -296,7 +296,7 @@ __device__ __forceinline__ void dkdv_exponents(float x[16], const f32x16_t& s, c
 
 template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
 __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
+  constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
   using TP = TilePair<T, D>;
@@ -505,7 +505,7 @@ constexpr int kSplitNW = 2 * kKB;
 
 template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
 __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArgs a) {
-  constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
+  constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
   using TP = TilePair<T, D, kSplitNW * 64>;
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
 // measured 1 % faster; the others keep the compiler's choice)
 template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
 __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
-  constexpr bool DROP = MODE == kBwdDrop, ALIBI = MODE == kBwdAlibi;
+  constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
   using TP = TilePair<T, D>;
@@ -959,7 +959,7 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
 #endif
   constexpr bool kSplit = D == 128 ? FA_BWD_SPLIT128 : FA_BWD_SPLIT64;
   const unsigned gq = (unsigned)a.nqb * nbh;
-  const int mode = a.drop_t ? kBwdDrop : (a.alibi ? kBwdAlibi : kBwdPlain);
+  const int mode = (a.drop_t ? kBwdDrop : 0) | (a.alibi ? kBwdAlibi : 0);
   auto launch2 = [&](auto mc, auto vc) {
     constexpr int M = decltype(mc)::value;
     constexpr bool V = decltype(vc)::value;
@@ -982,11 +982,14 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
   };
   using F = std::false_type;
   using Tr = std::true_type;
+  constexpr int kBoth = kBwdAlibi | kBwdDrop;
   if (varlen) {
+    if (mode == kBoth) return launch2(std::integral_constant<int, kBoth>{}, Tr{});
     if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{}, Tr{});
     if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{}, Tr{});
     return launch2(std::integral_constant<int, kBwdPlain>{}, Tr{});
   }
+  if (mode == kBoth) return launch2(std::integral_constant<int, kBoth>{}, F{});
   if (mode == kBwdDrop) return launch2(std::integral_constant<int, kBwdDrop>{}, F{});
   if (mode == kBwdAlibi) return launch2(std::integral_constant<int, kBwdAlibi>{}, F{});
   return launch2(std::integral_constant<int, kBwdPlain>{}, F{});

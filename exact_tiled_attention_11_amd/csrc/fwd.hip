@@ -664,15 +664,15 @@ struct PipeCfg {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-// MODE: kPipePlain, kPipeAlibi (ALiBi bias) or kPipeDrop (attention dropout),
+// MODE: bit flags kPipeAlibi (ALiBi bias) and kPipeDrop (attention dropout),
 // fixed-length or packed (a packed sequence's index takes the batch index's
-// place in the dropout counters).
+// place in the dropout counters); the prefix mask is a runtime value in all.
 constexpr int kPipePlain = 0, kPipeAlibi = 1, kPipeDrop = 2;
 
 template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN, int MODE>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdArgs a) {
-  constexpr bool ALIBI = MODE == kPipeAlibi;
-  constexpr bool DROP = MODE == kPipeDrop;
+  constexpr bool ALIBI = (MODE & kPipeAlibi) != 0;
+  constexpr bool DROP = (MODE & kPipeDrop) != 0;
   using C = PipeCfg<T, D, NW, PK>;
   using E = Elem<T>;
   using frag = typename E::frag;
@@ -1205,29 +1205,20 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
   if constexpr (UsePipe<T, D>::value) {
     constexpr int NW = 4, PK = D == 128 ? FA_PIPE_PK128 : FA_PIPE_PK64;
     constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
-    constexpr int P0 = kPipePlain, PA = kPipeAlibi, PD = kPipeDrop;
-    if (a.alibi) {
+    // one instance per (mode, causal, packed)
+    auto go = [&](auto mc) {
+      constexpr int M = decltype(mc)::value;
       if (causal) {
-        if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, PA>, grid, NW * 64, lds, stream, a);
-        return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PA>, grid, NW * 64, lds, stream, a);
+        if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, M>, grid, NW * 64, lds, stream, a);
+        return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, M>, grid, NW * 64, lds, stream, a);
       }
-      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, PA>, grid, NW * 64, lds, stream, a);
-      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, PA>, grid, NW * 64, lds, stream, a);
-    }
-    if (a.drop_t) {
-      if (causal) {
-        if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, PD>, grid, NW * 64, lds, stream, a);
-        return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, PD>, grid, NW * 64, lds, stream, a);
-      }
-      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, PD>, grid, NW * 64, lds, stream, a);
-      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, PD>, grid, NW * 64, lds, stream, a);
-    }
-    if (causal) {
-      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, true, P0>, grid, NW * 64, lds, stream, a);
-      return launch_k(fwd_pipe_kernel<T, D, NW, PK, true, false, P0>, grid, NW * 64, lds, stream, a);
-    }
-    if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, P0>, grid, NW * 64, lds, stream, a);
-    return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, P0>, grid, NW * 64, lds, stream, a);
+      if (varlen) return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, true, M>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_pipe_kernel<T, D, NW, PK, false, false, M>, grid, NW * 64, lds, stream, a);
+    };
+    if (a.alibi && a.drop_t) return go(IC<kPipeAlibi | kPipeDrop>{});
+    if (a.alibi) return go(IC<kPipeAlibi>{});
+    if (a.drop_t) return go(IC<kPipeDrop>{});
+    return go(IC<kPipePlain>{});
   }
   using Tl = Tile<T, D>;
   constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;

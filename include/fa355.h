@@ -278,7 +278,7 @@ FA355_API fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v
  * that sequence's keys [0, prefix), ALiBi distances are within the
  * sequence, and the dropout counters take the sequence index s in the
  * place of the batch index b.  fp16/bf16 only (fp32: FA_ERR_UNSUPPORTED);
- * ALiBi and dropout do not combine (there is no entry point for both).
+ * fa_fwd_varlen_ex / fa_bwd_varlen_ex below take all options together.
  * Arguments, layouts, workspaces, errors and ordering as fa_fwd_varlen /
  * fa_bwd_varlen plus, for the options, as fa_fwd_masked / fa_fwd_dropout;
  * a backward call must repeat the forward call's options.
@@ -317,6 +317,41 @@ FA355_API fa_status_t fa_bwd_varlen_dropout(const void* q, const void* k, const 
                                             float dropout_p, uint64_t seed, void* workspace,
                                             size_t workspace_bytes, fa_dtype_t dtype,
                                             void* stream);
+
+/*
+ * Every option at once: the prefix mask, ALiBi and dropout together (the
+ * guide's flash_attn and flash_attn_varlen calls take them together).  The
+ * entry points above are these with the other options off; the rules of
+ * each option, and the arguments, layouts, workspaces and errors, are those
+ * given there.  dropout_p = 0 is no dropout.  A backward call repeats the
+ * forward call's options.  fp16/bf16 for any option (fp32 with none only).
+ */
+FA355_API fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                                const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
+                                float dropout_p, uint64_t seed, fa_dtype_t dtype, void* stream);
+FA355_API fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                                const int32_t* seqlens_k, int prefix, const float* alibi_slopes,
+                                float dropout_p, uint64_t seed, void* workspace,
+                                size_t workspace_bytes, fa_dtype_t dtype, void* stream);
+FA355_API fa_status_t fa_fwd_varlen_ex(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                       int total_k, int H, int D, float scale, int causal,
+                                       int prefix, const float* alibi_slopes, float dropout_p,
+                                       uint64_t seed, void* workspace, size_t workspace_bytes,
+                                       fa_dtype_t dtype, void* stream);
+FA355_API fa_status_t fa_bwd_varlen_ex(const void* q, const void* k, const void* v,
+                                       const void* o, const float* lse, const void* dout,
+                                       void* dq, void* dk, void* dv, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                       int total_k, int max_seqlen_q, int max_seqlen_k, int H,
+                                       int D, float scale, int causal, int prefix,
+                                       const float* alibi_slopes, float dropout_p, uint64_t seed,
+                                       void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                                       void* stream);
 
 /* Static strings; never NULL. */
 FA355_API const char* fa_status_string(fa_status_t status);

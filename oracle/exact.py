@@ -167,13 +167,15 @@ def attention(q, k, v, scale, causal, seqlens_k=None, row_chunk=1024, prefix=0,
     return o, lse
 
 
-def attention_dropout(q, k, v, scale, causal, dropout_p, seed, seqlens_k=None, row_chunk=1024):
+def attention_dropout(q, k, v, scale, causal, dropout_p, seed, seqlens_k=None, row_chunk=1024,
+                      prefix=0, alibi_slopes=None):
     """Batched attention with attention dropout (BSHD layout), the form the
     HF integration guide's parameter table gives for training: dropout_p is
     the probability of dropping a weight.  The keep decisions and their
     scale are those of ``oracle.dropout`` (Philox4x32-10 counters per
-    (batch, head, query, 16-key group)).  Returns O [B, Nq, H, D] and the
-    undropped lse [B, H, Nq].
+    (batch, head, query, 16-key group)).  ``prefix`` and ``alibi_slopes``
+    add the mask families as in ``attention``.  Returns O [B, Nq, H, D] and
+    the undropped lse [B, H, Nq].
     """
     q = np.asarray(q)
     B, nq, H, D = q.shape
@@ -189,8 +191,9 @@ def attention_dropout(q, k, v, scale, causal, dropout_p, seed, seqlens_k=None, r
                 rows = np.arange(r0, r1)
                 keep = _dropout.keep_mask(seed, b, h, rows, lk, t)
                 ob, lb = attention_rows(q[b, r0:r1, h, :], rows, k[b, :, h, :], v[b, :, h, :],
-                                        nq, lk, scale, causal, keep=keep,
-                                        keep_scale=_dropout.keep_scale(t))
+                                        nq, lk, scale, causal, prefix,
+                                        None if alibi_slopes is None else alibi_slopes[h],
+                                        keep=keep, keep_scale=_dropout.keep_scale(t))
                 o[b, r0:r1, h, :] = ob
                 lse[b, h, r0:r1] = lb
     return o, lse

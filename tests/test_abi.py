@@ -29,7 +29,8 @@ def test_header_declares_the_api():
         "fa_bwd", "fa_bwd_dropout", "fa_bwd_masked", "fa_bwd_varlen", "fa_bwd_varlen_dropout",
         "fa_bwd_varlen_masked", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
         "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_dropout",
-        "fa_fwd_varlen_masked", "fa_fwd_varlen_workspace_bytes",
+        "fa_fwd_varlen_masked", "fa_fwd_varlen_workspace_bytes", "fa_fwd_ex", "fa_bwd_ex",
+        "fa_fwd_varlen_ex", "fa_bwd_varlen_ex",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
         "fa_version"])

@@ -1,6 +1,7 @@
-"""GPU parity of packed variable-length batches with the prefix mask, ALiBi
-and attention dropout (fa_fwd_varlen_masked / _dropout and fa_bwd_varlen_
-masked / _dropout through the C ABI) against the oracle's packed forms.
+"""GPU parity of the options together and on packed batches: the prefix
+mask, ALiBi and attention dropout through fa_fwd_varlen_masked / _dropout /
+_ex, fa_bwd_varlen_masked / _dropout / _ex, fa_fwd_ex and fa_bwd_ex, against
+the oracle.
 
 * Outputs and log-sum-exp against ``oracle.attention_varlen`` with the same
   options; gradients against ``oracle.attention_varlen_bwd``.  Ragged
@@ -61,6 +62,10 @@ CASES = [
      [300, 130, 33], dict(dropout=0.3)),
     ("bf16 D64 bidirectional dropout 0.5", "bf16", 64, 2, False, [64, 200, 5], [190, 7, 128],
      dict(dropout=0.5)),
+    ("bf16 D64 causal prefix+ALiBi+dropout", "bf16", 64, 3, True, [100, 260, 0, 33],
+     [100, 260, 0, 33], dict(prefix=40, alibi=True, dropout=0.2)),
+    ("f16 D128 causal ALiBi+dropout Lq != Lk", "f16", 128, 2, True, [100, 260, 33],
+     [300, 130, 33], dict(alibi=True, dropout=0.3)),
 ]
 
 
@@ -106,8 +111,9 @@ def test_forward_and_gradients(case):
     assert_grad_close(dtype, wl.to_f64(dv), rv, "%s dv" % name)
 
 
-@pytest.mark.parametrize("opt", [dict(prefix=50), dict(alibi=True), dict(dropout=0.25)],
-                         ids=["prefix", "alibi", "dropout"])
+@pytest.mark.parametrize("opt", [dict(prefix=50), dict(alibi=True), dict(dropout=0.25),
+                                 dict(prefix=50, alibi=True, dropout=0.25)],
+                         ids=["prefix", "alibi", "dropout", "all"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_equal_lengths_match_the_fixed_length_entry_points(opt, D):
     fa = _fa()
@@ -120,10 +126,8 @@ def test_equal_lengths_match_the_fixed_length_entry_points(opt, D):
     p = float(np.float32(opt.get("dropout", 0.0)))
     prefix = opt.get("prefix", 0)
     say("  packing %s D%d" % (sorted(opt), D))
-    if p:
-        of, lf = fa.fwd_dropout(q, k, v, dropout_p=p, seed=77, causal=True, scale=w.scale)
-    else:
-        of, lf = fa.fwd_masked(q, k, v, causal=True, scale=w.scale, prefix=prefix, alibi_slopes=sd)
+    of, lf = fa.fwd_ex(q, k, v, causal=True, scale=w.scale, prefix=prefix, alibi_slopes=sd,
+                       dropout_p=p, seed=77)
     gf = fa.bwd(q, k, v, of, lf, do, causal=True, scale=w.scale, prefix=prefix, alibi_slopes=sd,
                 dropout_p=p, seed=77)
     cu = torch.arange(B + 1, dtype=torch.int32, device="cuda") * L
@@ -138,3 +142,64 @@ def test_equal_lengths_match_the_fixed_length_entry_points(opt, D):
                        lv.view(torch.int32))
     for a, b in zip(gf, gv):
         assert torch.equal(pk(a).view(torch.int16), b.view(torch.int16))
+
+
+FIXED = [
+    # name, dtype, D, causal, B, H, Nq, Nk, seqlens, options
+    ("bf16 D64 causal prefix+ALiBi+dropout", "bf16", 64, True, 2, 3, 300, 300, None,
+     dict(prefix=70, alibi=True, dropout=0.2)),
+    ("f16 D128 causal ALiBi+dropout Nq300 Nk100", "f16", 128, True, 1, 2, 300, 100, None,
+     dict(alibi=True, dropout=0.3)),
+    ("bf16 D64 bidirectional ALiBi+dropout padded keys", "bf16", 64, False, 2, 2, 200, 333,
+     [333, 129], dict(alibi=True, dropout=0.4)),
+    ("bf16 D128 causal prefix+dropout", "bf16", 128, True, 2, 2, 257, 257, None,
+     dict(prefix=100, dropout=0.25)),
+]
+
+
+@pytest.mark.parametrize("case", FIXED, ids=lambda c: c[0])
+def test_fixed_length_every_option(case):
+    """fa_fwd_ex and fa_bwd_ex (the options together) against the oracle."""
+    name, dtype, D, causal, B, H, Nq, Nk, seqlens, opt = case
+    fa = _fa()
+    w = wl.Workload(name, "prefill", dtype, H=H, D=D, causal=causal, scale=1 / math.sqrt(D),
+                    seed=300 + len(name), B=B, Nq=Nq, Nk=Nk)
+    q, k, v = wl.prefill_inputs(w)
+    do = wl.tensor(w, 3, (B, Nq, H, D))
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            k[b, L:] = float("nan")
+            v[b, L:] = float("nan")
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device="cuda")
+    slopes = wl.alibi_slopes(H) if opt.get("alibi") else None
+    sd = None if slopes is None else torch.from_numpy(slopes).cuda()
+    prefix = opt.get("prefix", 0)
+    p = float(np.float32(opt.get("dropout", 0.0)))
+    seed = 5000 + len(name)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    outs = []
+    for rep in range(2):
+        say("  fa_fwd_ex + fa_bwd_ex %s rep %d" % (name, rep))
+        o, lse = fa.fwd_ex(qd, kd, vd, causal=causal, scale=w.scale, seqlens_k=sl, prefix=prefix,
+                           alibi_slopes=sd, dropout_p=p, seed=seed)
+        g = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, scale=w.scale, seqlens_k=sl,
+                   prefix=prefix, alibi_slopes=sd, dropout_p=p, seed=seed)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (o, lse, *g)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), "run-to-run difference"
+    o, lse, dq, dk, dv = outs[0]
+    if seqlens is not None:
+        for b, L in enumerate(seqlens):
+            assert (dk[b, L:] == 0).all() and (dv[b, L:] == 0).all()
+    o_ref, lse_ref = oracle.attention_dropout(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), w.scale,
+                                              causal, p, seed, seqlens_k=seqlens, prefix=prefix,
+                                              alibi_slopes=slopes)
+    ks = oracle.keep_scale(oracle.drop_threshold(p))
+    assert_close(dtype, wl.to_f64(o) / ks, o_ref / ks, lse.double().numpy(), lse_ref, name)
+    rq, rk, rv = oracle.attention_bwd(wl.to_f64(q), wl.to_f64(k), wl.to_f64(v), wl.to_f64(do),
+                                      w.scale, causal, seqlens_k=seqlens, dropout_p=p, seed=seed,
+                                      prefix=prefix, alibi_slopes=slopes)
+    assert_grad_close(dtype, wl.to_f64(dq), rq, "%s dq" % name)
+    assert_grad_close(dtype, wl.to_f64(dk), rk, "%s dk" % name)
+    assert_grad_close(dtype, wl.to_f64(dv), rv, "%s dv" % name)

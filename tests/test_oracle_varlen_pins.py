@@ -79,6 +79,8 @@ CASES = [
     ([6, 3], False, 0, True, 0.0),
     ([5, 6, 2], True, 0, False, 0.3),
     ([4, 5], False, 0, False, 0.5),
+    ([6, 4, 5], True, 2, True, 0.3),   # every option at once
+    ([5, 6], False, 0, True, 0.4),
 ]
 
 
@@ -112,10 +114,11 @@ OPTIONS = [
     dict(prefix=3),
     dict(alibi_slopes=np.array([0.5, 0.0625, 0.25])),
     dict(dropout_p=0.25, seed=99),
+    dict(prefix=5, alibi_slopes=np.array([0.5, 0.0625, 0.25]), dropout_p=0.25, seed=98),
 ]
 
 
-@pytest.mark.parametrize("opt", OPTIONS, ids=["prefix", "alibi", "dropout"])
+@pytest.mark.parametrize("opt", OPTIONS, ids=["prefix", "alibi", "dropout", "all"])
 @pytest.mark.parametrize("causal", [True, False])
 def test_equal_lengths_match_the_fixed_length_oracle(opt, causal):
     if "prefix" in opt and not causal:
@@ -129,7 +132,9 @@ def test_equal_lengths_match_the_fixed_length_oracle(opt, causal):
     pq, pk, pv, pdo = (t.reshape(B * L, H, D) for t in (q, k, v, do))
     o, lse = oracle.attention_varlen(pq, pk, pv, cu, cu, 0.35, causal, **opt)
     if "dropout_p" in opt:
-        of, lf = oracle.attention_dropout(q, k, v, 0.35, causal, opt["dropout_p"], opt["seed"])
+        masks = {n: opt[n] for n in ("prefix", "alibi_slopes") if n in opt}
+        of, lf = oracle.attention_dropout(q, k, v, 0.35, causal, opt["dropout_p"], opt["seed"],
+                                          **masks)
     else:
         of, lf = oracle.attention(q, k, v, 0.35, causal, **opt)
     np.testing.assert_allclose(o, of.reshape(B * L, H, D), rtol=0, atol=1e-13)
@@ -140,7 +145,7 @@ def test_equal_lengths_match_the_fixed_length_oracle(opt, causal):
         np.testing.assert_allclose(a, b.reshape(B * L, H, D), rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("opt", OPTIONS, ids=["prefix", "alibi", "dropout"])
+@pytest.mark.parametrize("opt", OPTIONS, ids=["prefix", "alibi", "dropout", "all"])
 def test_gradients_by_finite_differences(opt):
     lens, H, D = [4, 7], 3, 3
     q, k, v, cu = _packed(lens, H, D)
