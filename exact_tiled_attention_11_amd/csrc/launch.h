@@ -24,10 +24,10 @@ struct FwdArgs {
   int nqb;                 // fixed-length: query blocks per (batch, head)
   int total_q;             // varlen: lse row stride
   float c;                 // scale * log2(e)
-  // mask families (16-bit fixed-length prefill only; zero / null otherwise)
+  // mask families (16-bit prefill only; zero / null otherwise)
   int prefix;              // with causal: keys [0, prefix) are seen by every query
   const float* alibi;      // [H] slopes: score += -slope_h * |j - (i + Lk - Lq)|
-  // attention dropout (16-bit fixed-length prefill only; drop_t = 0: none)
+  // attention dropout (16-bit prefill only; drop_t = 0: none)
   uint32_t drop_t;         // a key is dropped when its random byte is below drop_t
   uint32_t seed_lo, seed_hi;
   float drop_scale;        // 256 / (256 - drop_t)
