@@ -359,3 +359,54 @@ def test_varlen_masked_and_dropout_validation():
     assert bdrop(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
     assert bdrop(ws=None) == fa.FA_ERR_WORKSPACE
     assert bdrop(tq=0, tk=0) == fa.FA_OK
+
+
+def test_every_option_entry_points_validation():
+    """fa_fwd_ex / fa_bwd_ex / fa_fwd_varlen_ex / fa_bwd_varlen_ex: each option's own checks,
+    before any HIP call."""
+    def fex(prefix=4, alibi=P, p=0.1, seed=3, dtype=fa.FA_BF16, causal=1, Nq=16):
+        return fa.fa_fwd_ex(P, P, P, P, P, 2, 4, Nq, 16, 64, 0.125, causal, None, prefix, alibi, p,
+                            seed, dtype, None)
+    assert fex(p=1.0) == fa.FA_ERR_INVALID_ARG
+    assert fex(prefix=-2) == fa.FA_ERR_INVALID_ARG
+    assert fex(causal=0) == fa.FA_ERR_INVALID_ARG            # prefix without causal
+    assert fex(alibi=P + 1) == fa.FA_ERR_INVALID_ARG
+    assert fex(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED      # options are 16-bit only
+    assert fex(dtype=fa.FA_F32, prefix=0, alibi=None, p=0.0, Nq=0) == fa.FA_OK
+    assert fex(Nq=0) == fa.FA_OK
+
+    def bex(p=0.2, **kw):
+        a = dict(B=1, H=2, Nq=8, Nk=8, D=128, causal=1, prefix=2, alibi=P, ws=P, wsb=1 << 20,
+                 dtype=fa.FA_F16)
+        a.update(kw)
+        return fa.fa_bwd_ex(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["Nq"], a["Nk"], a["D"],
+                            0.1, a["causal"], None, a["prefix"], a["alibi"], p, 5, a["ws"],
+                            a["wsb"], a["dtype"], None)
+    assert bex(p=-0.5) == fa.FA_ERR_INVALID_ARG
+    assert bex(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bex(ws=None) == fa.FA_ERR_WORKSPACE
+    assert bex(Nq=0, Nk=0) == fa.FA_OK
+
+    def fvx(p=0.1, **kw):
+        a = dict(prefix=3, alibi=P, causal=1, tq=10, dtype=fa.FA_BF16, ws=P)
+        a.update(kw)
+        return fa.fa_fwd_varlen_ex(P, P, P, P, P, P, P, 2, a["tq"], 10, 2, 64, 0.1, a["causal"],
+                                   a["prefix"], a["alibi"], p, 9, a["ws"], 1 << 20, a["dtype"],
+                                   None)
+    assert fvx(p=2.0) == fa.FA_ERR_INVALID_ARG
+    assert fvx(causal=0) == fa.FA_ERR_INVALID_ARG
+    assert fvx(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert fvx(ws=None) == fa.FA_ERR_WORKSPACE
+    assert fvx(tq=0) == fa.FA_OK
+
+    def bvx(p=0.1, **kw):
+        a = dict(prefix=3, alibi=P, tq=100, tk=100, dtype=fa.FA_BF16, wsb=1 << 20)
+        a.update(kw)
+        return fa.fa_bwd_varlen_ex(P, P, P, P, P, P, P, P, P, P, P, 2, a["tq"], a["tk"], 60, 60, 2,
+                                   64, 0.1, 1, a["prefix"], a["alibi"], p, 9, P, a["wsb"],
+                                   a["dtype"], None)
+    assert bvx(p=1.0) == fa.FA_ERR_INVALID_ARG
+    assert bvx(prefix=-1) == fa.FA_ERR_INVALID_ARG
+    assert bvx(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+    assert bvx(wsb=16) == fa.FA_ERR_WORKSPACE
+    assert bvx(tq=0, tk=0) == fa.FA_OK
