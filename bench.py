@@ -206,7 +206,10 @@ def run_config(n, args, dev):
         q, k, v = make_prefill(w, dev)
         do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D)).to(dev)
         sd = torch.from_numpy(wl.alibi_slopes(w.H)).to(dev) if w.alibi else None
-        if w.dropout:
+        if w.dropout and (w.prefix or w.alibi):
+            o, lse = fa.fwd_ex(q, k, v, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                               alibi_slopes=sd, dropout_p=w.dropout, seed=w.seed)
+        elif w.dropout:
             o, lse = fa.fwd_dropout(q, k, v, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
                                     scale=w.scale)
         elif w.prefix or w.alibi:
@@ -223,7 +226,12 @@ def run_config(n, args, dev):
         q, k, v = make_prefill(w, dev)
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
-        if w.dropout:
+        if w.dropout and (w.prefix or w.alibi):
+            sd = torch.from_numpy(wl.alibi_slopes(w.H)).to(dev) if w.alibi else None
+            call = lambda: fa.fwd_ex(q, k, v, causal=w.causal, scale=w.scale, prefix=w.prefix,
+                                     alibi_slopes=sd, dropout_p=w.dropout, seed=w.seed, out=o,
+                                     lse=lse)
+        elif w.dropout:
             call = lambda: fa.fwd_dropout(q, k, v, dropout_p=w.dropout, seed=w.seed,
                                           causal=w.causal, scale=w.scale, out=o, lse=lse)
         elif w.prefix or w.alibi:
@@ -238,13 +246,15 @@ def run_config(n, args, dev):
         do = wl.tensor(w, 3, tuple(q.shape)).to(dev)
         cud = torch.from_numpy(cu).to(dev)
         mx = int(np.diff(cu).max())
-        o, lse = fa.fwd_varlen(q, k, v, cud, cud, causal=w.causal, scale=w.scale)
+        sd = torch.from_numpy(wl.alibi_slopes(w.H)).to(dev) if w.alibi else None
+        opts = dict(prefix=w.prefix, alibi_slopes=sd, dropout_p=w.dropout, seed=w.seed)
+        o, lse = fa.fwd_varlen(q, k, v, cud, cud, causal=w.causal, scale=w.scale, **opts)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(fa.fa_bwd_workspace_bytes(1, w.H, q.shape[0]), dtype=torch.uint8,
                          device=dev)
         call = lambda: fa.bwd_varlen(q, k, v, o, lse, do, cud, cud, causal=w.causal,
                                      scale=w.scale, max_seqlen_q=mx, max_seqlen_k=mx, dq=dq,
-                                     dk=dk, dv=dv, workspace=ws)
+                                     dk=dk, dv=dv, workspace=ws, **opts)
     elif w.kind == "varlen":
         q, k, v, cu = wl.varlen_inputs(w)
         q, k, v = q.to(dev), k.to(dev), v.to(dev)
@@ -253,8 +263,10 @@ def run_config(n, args, dev):
         lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device=dev)
         ws = torch.empty(fa.fa_fwd_varlen_workspace_bytes(len(cu) - 1, q.shape[0]),
                          dtype=torch.uint8, device=dev)
+        sd = torch.from_numpy(wl.alibi_slopes(w.H)).to(dev) if w.alibi else None
         call = lambda: fa.fwd_varlen(q, k, v, cud, cud, causal=w.causal, scale=w.scale, out=o,
-                                     lse=lse, workspace=ws)
+                                     lse=lse, workspace=ws, prefix=w.prefix, alibi_slopes=sd,
+                                     dropout_p=w.dropout, seed=w.seed)
     elif w.kind == "paged":
         dq, kc, vc, sl = make_decode(w, dev)
         table, num_pages = wl.page_layout(w, w.page_size)
@@ -324,14 +336,17 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one call only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for HBM byte counters")
-    ap.add_argument("--config", type=int, choices=list(range(1, 15)), default=None,
+    ap.add_argument("--config", type=int, choices=list(range(1, 19)), default=None,
                     help="time one workload alone (its library call only) and print a JSON "
                          "line for it instead of the bench line: 1-5 the benchmark table, "
                          "6 its decode over a paged cache, 7 / 8 its N8192 causal prefill "
                          "with a 2048-key prefix mask / with ALiBi, 9 the gradients of "
                          "that prefill (fa_bwd), 10 / 11 that prefill / its gradients with "
                          "attention dropout 0.1, 12 / 13 the gradients with the prefix mask / "
-                         "with ALiBi, 14 the gradients of the varlen workload")
+                         "with ALiBi, 14 the gradients of the varlen workload, 15 / 16 the "
+                         "varlen workload with ALiBi and dropout 0.1 / its gradients, 17 / 18 "
+                         "the N8192 causal prefill with the prefix, ALiBi and dropout 0.1 / its "
+                         "gradients")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: libfa355 has no multi-GPU path "

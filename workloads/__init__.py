@@ -91,7 +91,7 @@ class Workload:
         if self.kind == "prefill":
             return self.B * _pairs(self.Nq, self.Nk, self.causal, self.prefix)
         if self.kind == "varlen":
-            return int(sum(_pairs(int(L), int(L), self.causal) for L in self.lengths()))
+            return int(sum(_pairs(int(L), int(L), self.causal, self.prefix) for L in self.lengths()))
         return int(self.lengths().sum())
 
     def bytes_moved(self) -> int:
@@ -157,6 +157,16 @@ CFG[13] = replace(CFG[8], name="backward causal bf16 B4 H16 N8192 D64 ALiBi", ba
 # Beyond the table: the gradients of the packed varlen prefill.
 CFG[14] = replace(CFG[4], name="backward varlen causal fp16 8 seqs U[1024,16384] H32 D128",
                   backward=True)
+
+# Beyond the table: the options together — the packed varlen prefill with
+# ALiBi and dropout 0.1 and its gradients; the N8192 causal prefill with the
+# 2048-key prefix, ALiBi and dropout 0.1 and its gradients.
+CFG[15] = replace(CFG[4], name="varlen causal fp16 8 seqs U[1024,16384] H32 D128 ALiBi dropout 0.1",
+                  alibi=True, dropout=0.1)
+CFG[16] = replace(CFG[15], name="backward " + CFG[15].name, backward=True)
+CFG[17] = replace(CFG[3], name="causal bf16 B4 H16 N8192 D64 prefix 2048 ALiBi dropout 0.1",
+                  prefix=2048, alibi=True, dropout=0.1)
+CFG[18] = replace(CFG[17], name="backward " + CFG[17].name, backward=True)
 
 # Beyond the table: the decode workload over a paged cache (16-row pages at
 # shuffled pool positions), the cache layout of serving runtimes.
