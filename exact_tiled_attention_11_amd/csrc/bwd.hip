@@ -188,9 +188,8 @@ struct BwdItem {
 template <bool VARLEN>
 __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a) {
   BwdItem w;
-  const int nbh = a.B * a.H;
-  w.blk = blockIdx.x / nbh;
-  const int bh = blockIdx.x - w.blk * nbh;
+  int bh;
+  block_coords(a.B * a.H, w.blk, bh);
   w.b = bh / a.H;
   w.h = bh - w.b * a.H;
   if constexpr (!VARLEN) {

@@ -85,6 +85,35 @@ __device__ __forceinline__ bool any_mask(uint64_t m) {
   return r != 0;
 }
 
+// (level, batch*head) coordinates of this workgroup in a grid of nlev * nbh
+// workgroups, level 0 the longest.  The eight XCDs take workgroups in turn
+// (workgroup i goes to XCD i mod 8), each XCD with its own L2.  When the
+// (batch, head) pairs divide evenly over the XCDs, XCD x takes the pairs x,
+// x+8, ... in groups of FA_XCD_GROUP, one group after another, and within a
+// group runs level by level over its pairs: an XCD then streams the K and V
+// (or Q and dO) of a few heads at a time, which stay in its L2 for the
+// workgroups that share them, while the longest blocks of a group still
+// start first.  Otherwise level l holds ids l*nbh .. l*nbh + nbh - 1.
+#ifndef FA_XCD_GROUP
+#define FA_XCD_GROUP 4
+#endif
+__device__ __forceinline__ void block_coords(int nbh, int& level, int& bh) {
+  const int i = blockIdx.x;
+  if (FA_XCD_GROUP > 0 && (nbh & 7) == 0) {
+    constexpr int g = FA_XCD_GROUP;
+    const int nlev = gridDim.x / nbh;
+    const int j = i >> 3;  // position in this XCD's sequence
+    const int grp = j / (g * nlev);
+    const int r = j - grp * (g * nlev);
+    const int gs = min(g, (nbh >> 3) - grp * g);  // pairs in this group (the last may have fewer)
+    level = r / gs;
+    bh = (grp * g + (r - level * gs)) * 8 + (i & 7);
+  } else {
+    level = i / nbh;
+    bh = i - level * nbh;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -154,9 +154,8 @@ struct WorkItem {
 template <bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
   if constexpr (!VARLEN) {
-    const int nbh = a.B * a.H;
-    const int level = blockIdx.x / nbh;
-    const int bh = blockIdx.x - level * nbh;
+    int level, bh;
+    block_coords(a.B * a.H, level, bh);
     w.qblk = CAUSAL ? (a.nqb - 1 - level) : level;
     const int b = bh / a.H;
     w.b = b;
