@@ -97,10 +97,11 @@ __device__ __forceinline__ bool any_mask(uint64_t m) {
 #ifndef FA_XCD_GROUP
 #define FA_XCD_GROUP 4
 #endif
+template <int G = FA_XCD_GROUP>
 __device__ __forceinline__ void block_coords(int nbh, int& level, int& bh) {
   const int i = blockIdx.x;
-  if (FA_XCD_GROUP > 0 && (nbh & 7) == 0) {
-    constexpr int g = FA_XCD_GROUP;
+  if (G > 0 && (nbh & 7) == 0) {
+    constexpr int g = G;
     const int nlev = gridDim.x / nbh;
     const int j = i >> 3;  // position in this XCD's sequence
     const int grp = j / (g * nlev);

@@ -151,6 +151,9 @@ struct WorkItem {
   int b, h, qblk, lq, lk;
   long long q_tok0, k_tok0, lse_base;
 };
+#ifndef FA_XCD_GROUP_VARLEN
+#define FA_XCD_GROUP_VARLEN 1
+#endif
 template <bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
   if constexpr (!VARLEN) {
@@ -167,8 +170,9 @@ __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
     w.k_tok0 = (long long)b * a.Nk;
     w.lse_base = ((long long)b * a.H + w.h) * a.Nq;
   } else {
-    const int t = blockIdx.x / a.H;
-    w.h = blockIdx.x - t * a.H;
+    int t, h;
+    block_coords<FA_XCD_GROUP_VARLEN>(a.H, t, h);
+    w.h = h;
     if (t >= a.sched[0]) return false;
     const int* tl = a.sched + 2 + 4 * a.nseq + 2 * t;
     const int s = tl[0];
@@ -1055,9 +1059,16 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
 }
 
 // ---------------------------------------------------------------------------
-// Varlen schedule: one workgroup sorts the (sequence, query block) tiles by
-// their number of key tiles, longest first (counting sort over LDS bins).
+// Varlen schedule, written by one workgroup: the (sequence, query block)
+// tiles sequence by sequence, each sequence's longest first.  The forward
+// grid walks it per head on each XCD, so the workgroups an XCD runs at once
+// share the K and V of one or two sequences in its L2.  (FA_VARLEN_SEQ_MAJOR
+// 0: all tiles sorted by their number of key tiles, longest first, by a
+// counting sort over LDS bins.)
 // ---------------------------------------------------------------------------
+#ifndef FA_VARLEN_SEQ_MAJOR
+#define FA_VARLEN_SEQ_MAJOR 1
+#endif
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 1024;
 
@@ -1087,6 +1098,41 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     seq[4 * s + 3] = k1 - k0;
   }
   __syncthreads();
+  if constexpr (FA_VARLEN_SEQ_MAJOR) {
+    // the tiles of sequence 0, then of sequence 1, ...; within a sequence the
+    // longest first.  Offsets: an exclusive scan of the tile counts, taken
+    // kSchedThreads sequences at a time.
+    int* part = scan;
+    static_assert(kSchedBins == kSchedThreads, "the scan buffer holds one count per thread");
+    int carry = 0;  // tiles of the sequences before this chunk (the same in every thread)
+    for (int base = 0; base < nseq; base += kSchedThreads) {
+      const int s = base + tid;
+      const int n = s < nseq ? (seq[4 * s + 1] + rows - 1) / rows : 0;
+      part[tid] = n;
+      __syncthreads();
+      for (int st = 1; st < kSchedThreads; st <<= 1) {
+        const int v = tid >= st ? part[tid - st] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+      }
+      const int first = carry + part[tid] - n;
+      for (int i = 0; i < n; ++i) {
+        const int pos = first + i;
+        if (pos < max_tiles) {
+          tiles[2 * pos] = s;
+          tiles[2 * pos + 1] = causal ? n - 1 - i : i;  // causal: the last query block sees the most keys
+        }
+      }
+      carry += part[kSchedThreads - 1];
+      __syncthreads();  // every thread has read part before the next chunk writes it
+    }
+    if (tid == 0) {
+      sched[0] = min(carry, max_tiles);
+      sched[1] = 0;
+    }
+    return;
+  }
   for (int s = tid; s < nseq; s += kSchedThreads) {
     const int lq = seq[4 * s + 1], lk = seq[4 * s + 3];
     const int nqb = (lq + rows - 1) / rows;

@@ -46,8 +46,8 @@ hipError_t launch_fwd(const FwdArgs& a, fa_dtype_t dtype, int D, bool causal, bo
 //   sched[0]                 number of tiles T
 //   sched[2 + 4s .. 5 + 4s]  sequence s: first q row, q rows, first k row, k rows
 //                            (clamped to [0, total_q] / [0, total_k])
-//   sched[2 + 4*nseq + 2t]   tile t: sequence, query block; tiles sorted by
-//                            descending number of key tiles (longest first)
+//   sched[2 + 4*nseq + 2t]   tile t: sequence, query block; tiles sequence by
+//                            sequence, each sequence's longest first
 hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int nseq,
                                   int total_q, int total_k, int rows, int key_tile,
                                   int causal, int max_tiles, int32_t* sched,
