@@ -145,6 +145,10 @@ VARLEN = [
                         lens_fixed=[0, 5, 0, 300, 1, 129, 0]),
     dataclasses.replace(wl.SMALL[4], name="varlen f32 D64 causal", dtype="f32", D=64, seed=13,
                         nseq=3),
+    # more sequences than the schedule kernel's threads: its tile-offset scan
+    # runs over three chunks of sequences, some of them empty
+    dataclasses.replace(wl.SMALL[4], name="varlen 2500 short sequences", dtype="bf16", D=64, H=2,
+                        nseq=2500, len_lo=0, len_hi=40, seed=14),
 ]
 
 
