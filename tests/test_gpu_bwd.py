@@ -98,6 +98,10 @@ BWD = [
     (P("bf16 D128 causal B2 H2 N300 padded keys", "bf16", 128, True, 2, 2, 300, 300, 153), [300, 40]),
     (P("f16 D128 noncausal B2 H1 Nq70 Nk390 padded keys", "f16", 128, False, 2, 1, 70, 390, 154),
      [390, 129]),
+    # B*H a multiple of 8: each XCD walks its (batch, head) pairs in groups of four (4+1, 4+2)
+    (P("bf16 D64 causal B5 H8 N300 (pair groups 4+1)", "bf16", 64, True, 5, 8, 300, 300, 60), None),
+    (P("f16 D128 causal B3 H16 N200 (pair groups 4+2)", "f16", 128, True, 3, 16, 200, 200, 155),
+     None),
 ]
 
 

@@ -96,6 +96,10 @@ PREFILL = [
     P("bf16 D64 noncausal Nk65", "bf16", 64, False, 1, 2, 64, 65),
     P("bf16 D64 scale 0", "bf16", 64, True, 1, 2, 100, 100, scale=0.0),
     P("bf16 D64 Nk0", "bf16", 64, False, 1, 2, 40, 0),
+    # B*H a multiple of 8: each XCD walks its (batch, head) pairs in groups of
+    # four, here four then one (40 pairs) and four then two (48)
+    P("bf16 D64 causal B5 H8 N300 (pair groups 4+1)", "bf16", 64, True, 5, 8, 300, 300),
+    P("f16 D128 causal B3 H16 N200 (pair groups 4+2)", "f16", 128, True, 3, 16, 200, 200),
 ]
 
 
