@@ -304,22 +304,85 @@ def _check(fn: str, status: int) -> None:
         raise FaError(fn, status)
 
 
-def fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
-        out=None, lse=None, return_lse: bool = True, stream=None) -> Tuple:
-    """Fixed-length attention. q [B, Nq, H, D]; k, v [B, Nk, H, D] -> (o, lse [B, H, Nq])."""
+def _expect(t, name: str, shape, dtype, device=None) -> None:
+    """Raise ValueError unless tensor t (if given) has this shape, dtype and device.  The
+    kernels address every buffer from the sizes of q (and k), so a mismatch would make them
+    read or write past an allocation."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError("%s must be %s of shape %s, got %s of shape %s"
+                         % (name, dtype, list(shape), t.dtype, list(t.shape)))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+
+
+def _index(t, name: str, n: int, device) -> None:
+    """int32 index vector of n entries (cu_seqlens, seqlens_k)."""
     import torch
+    if t is None:
+        return
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != n:
+        raise ValueError("%s must be int32 of shape [%d], got %s of shape %s"
+                         % (name, n, t.dtype, list(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+
+
+def _check_fixed(q, k, v, seqlens_k, alibi_slopes, out, lse):
+    """Shapes of a fixed-length call: q [B,Nq,H,D], k and v [B,Nk,H,D] of q's dtype."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
     B, Nq, H, D = q.shape
     Nk = k.shape[1]
     if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
+    _expect(k, "k", k.shape, q.dtype, q.device)
+    _expect(v, "v", k.shape, q.dtype, q.device)
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    _index(seqlens_k, "seqlens_k", B, q.device)
+    _expect(alibi_slopes, "alibi_slopes", (H,), torch.float32, q.device)
+    return B, Nq, H, D, Nk
+
+
+def _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k, alibi_slopes, out, lse):
+    """Shapes of a packed call: q [total_q,H,D], k and v [total_k,H,D] of q's dtype, int32
+    cu_seqlens of equal length."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be [total_q,H,D], [total_k,H,D], [total_k,H,D] of one dtype")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    if k.shape != (total_k, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be [total_q,H,D], [total_k,H,D], [total_k,H,D] of one dtype")
+    _expect(k, "k", k.shape, q.dtype, q.device)
+    _expect(v, "v", k.shape, q.dtype, q.device)
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q must be int32 of shape [nseq + 1]")
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    _index(cu_seqlens_q, "cu_seqlens_q", nseq + 1, q.device)
+    _index(cu_seqlens_k, "cu_seqlens_k", nseq + 1, q.device)
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (H, total_q), torch.float32, q.device)
+    _expect(alibi_slopes, "alibi_slopes", (H,), torch.float32, q.device)
+    return total_q, H, D, total_k, nseq
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seqlens_k=None,
+        out=None, lse=None, return_lse: bool = True, stream=None) -> Tuple:
+    """Fixed-length attention. q [B, Nq, H, D]; k, v [B, Nk, H, D] -> (o, lse [B, H, Nq])."""
+    import torch
+    B, Nq, H, D, Nk = _check_fixed(q, k, v, seqlens_k, None, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
-        raise ValueError("seqlens_k must be int32[B]")
     st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D, float(scale),
                 int(bool(causal)), _ptr(seqlens_k), _dtype_code(q), _stream(stream))
     _check("fa_fwd", st)
@@ -331,20 +394,13 @@ def fwd_masked(q, k, v, *, causal: bool = False, scale: Optional[float] = None, 
                stream=None) -> Tuple:
     """fwd with the prefix mask (causal only) and/or ALiBi slopes (float32 [H] on the device)."""
     import torch
-    B, Nq, H, D = q.shape
-    Nk = k.shape[1]
-    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
-    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H):
-        raise ValueError("alibi_slopes must be float32[H]")
+    B, Nq, H, D, Nk = _check_fixed(q, k, v, seqlens_k, alibi_slopes, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
-        raise ValueError("seqlens_k must be int32[B]")
     st = fa_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D,
                        float(scale), int(bool(causal)), _ptr(seqlens_k), int(prefix),
                        _ptr(alibi_slopes), _dtype_code(q), _stream(stream))
@@ -357,18 +413,13 @@ def fwd_dropout(q, k, v, *, dropout_p: float, seed: int, causal: bool = False,
                 return_lse: bool = True, stream=None) -> Tuple:
     """fwd with attention dropout (training): keep decisions from Philox4x32-10 keyed by seed."""
     import torch
-    B, Nq, H, D = q.shape
-    Nk = k.shape[1]
-    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
+    B, Nq, H, D, Nk = _check_fixed(q, k, v, seqlens_k, None, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
-        raise ValueError("seqlens_k must be int32[B]")
     st = fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D,
                         float(scale), int(bool(causal)), _ptr(seqlens_k), float(dropout_p),
                         int(seed) & 0xFFFFFFFFFFFFFFFF, _dtype_code(q), _stream(stream))
@@ -382,14 +433,7 @@ def fwd_ex(q, k, v, *, causal: bool = False, scale: Optional[float] = None, seql
     """fwd with every option at once: the prefix mask (causal only), ALiBi slopes (float32 [H]
     on the device) and attention dropout (fp16/bf16 for any option)."""
     import torch
-    B, Nq, H, D = q.shape
-    Nk = k.shape[1]
-    if k.shape != (B, Nk, H, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must be [B,Nq,H,D], [B,Nk,H,D], [B,Nk,H,D] of one dtype")
-    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H):
-        raise ValueError("alibi_slopes must be float32[H]")
-    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B):
-        raise ValueError("seqlens_k must be int32[B]")
+    B, Nq, H, D, Nk = _check_fixed(q, k, v, seqlens_k, alibi_slopes, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -411,8 +455,14 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] =
     (with dropout_p > 0: for fwd_dropout with the same dropout_p and seed; with prefix or
     alibi_slopes: for fwd_masked with the same ones; with both: for fwd_ex)."""
     import torch
-    B, Nq, H, D = q.shape
-    Nk = k.shape[1]
+    B, Nq, H, D, Nk = _check_fixed(q, k, v, seqlens_k, alibi_slopes, None, lse)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(dout, "dout", q.shape, q.dtype, q.device)
+    _expect(dq, "dq", q.shape, q.dtype, q.device)
+    _expect(dk, "dk", k.shape, q.dtype, q.device)
+    _expect(dv, "dv", k.shape, q.dtype, q.device)
+    if lse is None or o is None or dout is None:
+        raise ValueError("o, lse and dout of the forward call are required")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq = torch.empty_like(q) if dq is None else dq
@@ -421,9 +471,6 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: Optional[float] =
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_bytes(B, H, Nq), 16), dtype=torch.uint8,
                                 device=q.device)
-    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or
-                                     alibi_slopes.numel() != H):
-        raise ValueError("alibi_slopes must be float32[H]")
     if dropout_p and (prefix or alibi_slopes is not None):
         st = fa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                        _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
@@ -461,11 +508,8 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
     prefix / alibi_slopes (float32 [H] on the device) select fa_fwd_varlen_masked, dropout_p > 0
     fa_fwd_varlen_dropout (positions and dropout counters per sequence)."""
     import torch
-    total_q, H, D = q.shape
-    total_k = k.shape[0]
-    nseq = cu_seqlens_q.numel() - 1
-    if cu_seqlens_k.numel() != nseq + 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    total_q, H, D, total_k, nseq = _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k,
+                                                 alibi_slopes, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -475,8 +519,6 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
     need = fa_fwd_varlen_workspace_bytes(max(nseq, 1), total_q)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H):
-        raise ValueError("alibi_slopes must be float32[H]")
     common = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
               _ptr(cu_seqlens_k), nseq, total_q, total_k, H, D, float(scale), int(bool(causal)))
     tail = (_ptr(workspace), workspace.numel(), _dtype_code(q), _stream(stream))
@@ -506,11 +548,15 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, *, causal: boo
     max_seqlen_q / max_seqlen_k default to the longest ranges of cu_seqlens (read on the host:
     pass them to avoid that synchronisation)."""
     import torch
-    total_q, H, D = q.shape
-    total_k = k.shape[0]
-    nseq = cu_seqlens_q.numel() - 1
-    if cu_seqlens_k.numel() != nseq + 1:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    total_q, H, D, total_k, nseq = _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k,
+                                                 alibi_slopes, None, lse)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(dout, "dout", q.shape, q.dtype, q.device)
+    _expect(dq, "dq", q.shape, q.dtype, q.device)
+    _expect(dk, "dk", k.shape, q.dtype, q.device)
+    _expect(dv, "dv", k.shape, q.dtype, q.device)
+    if lse is None or o is None or dout is None:
+        raise ValueError("o, lse and dout of the forward call are required")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if max_seqlen_q is None:
@@ -548,8 +594,17 @@ def decode_splitkv(q, k_cache, v_cache, seqlens_k, *, scale: Optional[float] = N
                    workspace=None, stream=None) -> Tuple:
     """Split-KV decode. q [B, H, D]; caches [B, Nk_max, H, D] -> (o [B, H, D], lse [B, H])."""
     import torch
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B,H,D] and the caches [B,Nk_max,H,D]")
     B, H, D = q.shape
     Nk_max = k_cache.shape[1]
+    _expect(k_cache, "k_cache", (B, Nk_max, H, D), q.dtype, q.device)
+    _expect(v_cache, "v_cache", (B, Nk_max, H, D), q.dtype, q.device)
+    if seqlens_k is None:
+        raise ValueError("seqlens_k is required")
+    _index(seqlens_k, "seqlens_k", B, q.device)
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, H), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -572,9 +627,20 @@ def decode_splitkv_paged(q, k_pages, v_pages, seqlens_k, block_table, *,
     """Split-KV decode over a paged cache. q [B, H, D]; pages [num_pages, page_size, H, D];
     block_table int32 [B, max_pages] -> (o [B, H, D], lse [B, H])."""
     import torch
+    if q.dim() != 3 or k_pages.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [B,H,D], the pages [num_pages,page_size,H,D] and "
+                         "block_table [B,max_pages]")
     B, H, D = q.shape
     num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
     max_pages = block_table.shape[1]
+    _expect(k_pages, "k_pages", (num_pages, page_size, H, D), q.dtype, q.device)
+    _expect(v_pages, "v_pages", (num_pages, page_size, H, D), q.dtype, q.device)
+    _expect(block_table, "block_table", (B, max_pages), torch.int32, q.device)
+    if seqlens_k is None:
+        raise ValueError("seqlens_k is required")
+    _index(seqlens_k, "seqlens_k", B, q.device)
+    _expect(out, "out", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, H), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:

@@ -55,6 +55,14 @@ extern "C" {
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype_t;
 
+/*
+ * Status codes.  They map the error catalog of the Hugging Face
+ * Flash-Attention-2 integration guide (section 常见错误排查: an unsupported
+ * dtype, an unsupported head_dim, a GPU the kernels do not run on): dtype and
+ * head_dim -> FA_ERR_UNSUPPORTED, device -> FA_ERR_HIP.  Arguments the guide's
+ * calls would reject as malformed -> FA_ERR_INVALID_ARG; a caller workspace
+ * that is too small -> FA_ERR_WORKSPACE.
+ */
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned pointer, non-finite scale */
