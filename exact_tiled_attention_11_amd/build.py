@@ -64,5 +64,36 @@ def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
     return out
 
 
+# Host-side AddressSanitizer build of the C ABI layer (argument validation,
+# dispatch), CPU only: api.cpp is compiled by g++ with the sanitizer and linked
+# with the device objects of the normal build, which stay uninstrumented.  Load
+# it with the sanitizer runtime preloaded (see asan_runtime()).
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libfa355_asan.so")
+HOST_ASAN = ["-fsanitize=address", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of g++'s AddressSanitizer runtime (for LD_PRELOAD)."""
+    return _run(["g++", "-print-file-name=libasan.so"]).strip()
+
+
+def build_asan() -> str:
+    objs = [os.path.join(BUILD, "libfa355.so.objs", s + ".o") for s in SOURCES if s != "api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    api = os.path.join(ASAN_DIR, "api.o")
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC"] + HOST_ASAN +
+         ["-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + INCLUDE, "-I" + CSRC,
+          "-c", os.path.join(CSRC, "api.cpp"), "-o", api])
+    _run(["g++", "-shared", "-o", ASAN_LIB, api] + objs +
+         ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"])
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan())
+    else:
+        print(build(verbose="-v" in sys.argv))
