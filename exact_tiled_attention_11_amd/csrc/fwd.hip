@@ -659,8 +659,16 @@ struct PipeCfg {
   static constexpr int kNS = PK + 2;
   static constexpr int kVBase = kNS * kSlotB;      // byte offset of the V ring
   static constexpr int kLdsB = 2 * kNS * kSlotB;
-  static constexpr int kLPS = kBC * kCPR / (64 * NW);  // 16-byte loads per lane per block
-  static_assert(kBC * kCPR % (64 * NW) == 0, "a block divides evenly over the lanes");
+  // The 16-byte chunks of a K (or V) block are spread over the lanes.  When a
+  // block has fewer chunks than the workgroup has lanes, waves 0 .. kKW-1
+  // load K and waves kKW .. 2 kKW-1 load V (the rest load nothing);
+  // otherwise every wave loads part of both.
+  static constexpr int kChunksBlk = kBC * kCPR;
+  static constexpr bool kSplitKV = kChunksBlk < 64 * NW;
+  static constexpr int kKW = kSplitKV ? kChunksBlk / 64 : NW;  // waves sharing one block
+  static constexpr int kLPS = kChunksBlk / (64 * kKW);        // 16-byte loads per lane per block
+  static_assert(kChunksBlk % (64 * kKW) == 0 && (!kSplitKV || 2 * kKW <= NW),
+                "a block divides evenly over the lanes");
   static_assert(kCPR >= 8, "swizzle needs at least 8 chunks per row");
 };
 
@@ -735,10 +743,15 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
 
   // this lane's 16-byte chunk of a block: row r, LDS position pos (global
   // chunk pos ^ swizzle(r))
+  constexpr int KW = C::kKW;
+  // this wave's part in the block loads: K, V or both (uniform)
+  const bool loads_k = !C::kSplitKV || wave < KW;
+  const bool loads_v = !C::kSplitKV || (wave >= KW && wave < 2 * KW);
+  const int lw = C::kSplitKV ? wave % KW : wave;  // position among the waves loading a block
   unsigned voffk[LPS], voffv[LPS];
 #pragma unroll
   for (int l = 0; l < LPS; ++l) {
-    const int p = (l * NW + wave) * 64 + lane;
+    const int p = (l * KW + lw) * 64 + lane;
     const int r = p / C::kCPR, pos = p % C::kCPR;
     voffk[l] = (unsigned)r * rsb + (unsigned)((pos ^ swz_k<C::kCPR>(r)) * 16);
     voffv[l] = (unsigned)r * rsb + (unsigned)((pos ^ swz_v<C::kCPR>(r)) * 16);
@@ -754,13 +767,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     const u32x4_t rsrc = make_rsrc(base + (size_t)(u > 0 ? u : 0) * C::kBC * rsb, (unsigned)rows * rsb);
 #pragma unroll
     for (int l = 0; l < LPS; ++l)
-      dma16(rsrc, voff[l], __builtin_amdgcn_readfirstlane(lds0 + slot + (l * NW + wave) * 1024));
+      dma16(rsrc, voff[l], __builtin_amdgcn_readfirstlane(lds0 + slot + (l * KW + lw) * 1024));
   };
   // step s (s = r mod kNS) requests K of block s+PK+1, then V of block s+PK
   auto issue = [&](int s, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
-    load(kp, voffk, s + PK + 1, kslot(r + PK + 1));
-    load(vp, voffv, s + PK, vslot(r + PK));
+    if (loads_k) load(kp, voffk, s + PK + 1, kslot(r + PK + 1));
+    if (loads_v) load(vp, voffv, s + PK, vslot(r + PK));
   };
 
   for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
@@ -783,6 +796,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
   float mrow = -INFINITY;  // running offset (units of scale*log2 e); -inf: no key yet
   float lrow = 0.f;        // running sum over this lane's keys
+  float negm = 0.f;        // -mrow, 0 while the row has seen no key
+  float thr = -1.f;        // a block sum above this settles: 2^15, or -1 while fresh
   __syncthreads();         // LDS zeroed before any block lands
 
   int klane[KS];
@@ -878,9 +893,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // lazy offset: raise m only if a probability could exceed 2^15 or the row
   // has seen no key yet; then rescale O and l and redo the block
   auto settle = [&](float ts) __attribute__((always_inline)) {
-    // one ballot per compare, or-ed as scalar masks
-    const uint64_t need = __builtin_amdgcn_ballot_w64(mrow == -INFINITY) |
-                          __builtin_amdgcn_ballot_w64(!(ts <= 0x1p15f));
+    // thr is -1 while the row has seen no key, so one compare covers both cases
+    const uint64_t need = __builtin_amdgcn_ballot_w64(!(ts <= thr));
     if (any_mask(need)) {
       float m = -INFINITY;
 #pragma unroll
@@ -894,6 +908,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
       const float mold = fresh ? 0.f : mrow;
       const float alpha = fresh ? 0.f : fast_exp2(-delta);
       mrow = (fresh && none) ? -INFINITY : mold + delta;
+      negm = (fresh && none) ? 0.f : -mrow;
+      thr = (fresh && none) ? -1.f : 0x1p15f;
       lrow *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
@@ -917,14 +933,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
     if constexpr (DROP) keep_words_rows(kw, 2 * u, hh, wq0 + col, wi.h, wi.b, a.seed_lo, a.seed_hi);
-    const float ms = mrow == -INFINITY ? 0.f : mrow;
+    float addend = negm;
     // ALiBi: -slope * |key - position| in exp2 units, key 8*(r>>2) + 4*hh +
     // (r&3) of the block, position qi + off.  In a causal block left of the
     // wave's first row every key is at or before the position, so the bias is
     // slope * (key - position): a per-lane part joins the exponent's addend
     // and the per-element part slope * (8*(r>>2) + (r&3)) is one FMA with a
     // literal.  Other blocks take the absolute value (two operations).
-    float addend = -ms;
     bool lin = false;
     float dbase = 0.f;
     if constexpr (ALIBI) {
@@ -973,8 +988,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     };
     float ts = 0.f;
     auto acc2 = [&](int c) __attribute__((always_inline)) {
-      ts += pe[2 * c];
-      ts += pe[2 * c + 1];
+      if (c == 0) {
+        ts = pe[0] + pe[1];
+      } else {
+        ts += pe[2 * c];
+        ts += pe[2 * c + 1];
+      }
       float p0 = pe[2 * c], p1 = pe[2 * c + 1];
       drop2(c, p0, p1);
       u32x4_t w = __builtin_bit_cast(u32x4_t, pk[c >> 2]);
@@ -1012,7 +1031,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // of u+1 and the softmax of u.  The scores of u+1 on a wave's last block
   // are computed and never used.
   auto step = [&](int u, auto rc) __attribute__((always_inline)) {
-    vm_wait<(2 * PK - 1) * LPS>();  // later requests (V of u, and PK-1 steps' worth) may stay pending
+    // K u+1 and V u-1 of this wave's part must be in: later requests (V of u
+    // and PK-1 steps' worth) may stay pending
+    if constexpr (!C::kSplitKV) vm_wait<(2 * PK - 1) * LPS>();
+    else if (loads_k) vm_wait<(PK - 1) * LPS>();
+    else if (loads_v) vm_wait<PK * LPS>();
     __syncthreads();        // every wave's part is in; the slots of K u and V u-2 are free
     issue(u, rc);
     // At u = nw every key of the block is hidden from this wave's rows (it
@@ -1025,7 +1048,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   [&]<int... S>(std::integer_sequence<int, S...>) {
     (issue(S - PK - 1, IC<(S - PK - 1 + 4 * C::kNS) % C::kNS>{}), ...);
   }(std::make_integer_sequence<int, PK + 1>{});
-  vm_wait<(2 * PK + 1) * LPS>();  // K of block 0 is in
+  if constexpr (!C::kSplitKV) vm_wait<(2 * PK + 1) * LPS>();  // K of block 0 is in
+  else if (loads_k) vm_wait<PK * LPS>();
   __syncthreads();
   if (nw > 0) scores0();
   // steps 0 .. nst, unrolled by kNS so every slot offset is a constant (the
@@ -1240,15 +1264,23 @@ template <typename T, int D>
 struct UsePipe {
   static constexpr bool value = FA_PIPE && sizeof(T) == 2;
 };
-static_assert(Tile<__bf16, 64>::QB == 1 && Tile<__bf16, 64>::NW == 4 &&
-              Tile<__bf16, 128>::QB == 1 && Tile<__bf16, 128>::NW == 4,
-              "pipelined kernel rows per workgroup must match the dispatch tables");
+#ifndef FA_PIPE_NW64
+#define FA_PIPE_NW64 4
+#endif
+#ifndef FA_PIPE_NW128
+#define FA_PIPE_NW128 4
+#endif
+// waves (of 32 query rows each) per workgroup of the pipelined kernel
+template <int D>
+struct PipeNW {
+  static constexpr int value = D == 64 ? FA_PIPE_NW64 : FA_PIPE_NW128;
+};
 
 template <typename T, int D>
 static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned grid,
                            hipStream_t stream) {
   if constexpr (UsePipe<T, D>::value) {
-    constexpr int NW = 4, PK = D == 128 ? FA_PIPE_PK128 : FA_PIPE_PK64;
+    constexpr int NW = PipeNW<D>::value, PK = D == 128 ? FA_PIPE_PK128 : FA_PIPE_PK64;
     constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
     // one instance per (mode, causal, packed)
     auto go = [&](auto mc) {
@@ -1278,6 +1310,7 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
 }
 
 template <typename T, int D> static int rows_t() {
+  if constexpr (UsePipe<T, D>::value) return PipeNW<D>::value * 32;
   return (Tile<T, D>::KSPLIT ? 1 : Tile<T, D>::NW) * 32 * Tile<T, D>::QB;
 }
 template <typename T, int D> static int keys_t() { return 32 * Tile<T, D>::KB; }

@@ -3,7 +3,8 @@
 The oracle cannot finish whole workloads of this size in a test, so each case compares sampled
 output rows (chosen at random plus tile boundaries and the first/last rows) with the oracle
 computed row by row, and checks properties that hold at any size on every row: all outputs
-finite, every causal row has a finite log-sum-exp, and two runs are bit-identical.
+finite (the output buffers start filled with NaN, so this also shows every element was written),
+every causal row has a finite log-sum-exp, and two runs are bit-identical.
 """
 
 import math
@@ -30,6 +31,17 @@ def _fa():
     return fa
 
 
+def nan_like(t, shape=None, dtype=None):
+    """An output buffer filled with NaN: after the call, an all-finite check over it
+    shows that the kernel wrote every element."""
+    return torch.full(t.shape if shape is None else shape, float("nan"),
+                      dtype=t.dtype if dtype is None else dtype, device=t.device)
+
+
+def nan_grads(q, k):
+    return dict(dq=nan_like(q), dk=nan_like(k), dv=nan_like(k))
+
+
 def _sample_rows(rng, n, extra=()):
     base = {0, 1, n - 1, n // 2}
     for t in (63, 64, 127, 128, 255, 256, 511, 512):
@@ -51,10 +63,11 @@ def test_prefill_full_size_sampled(cfg):
     sd = None if slopes is None else torch.from_numpy(slopes).cuda()
 
     def call():
+        outs = dict(out=nan_like(qd), lse=nan_like(qd, (w.B, w.H, w.Nq), torch.float32))
         if w.prefix or w.alibi:
             return fa.fwd_masked(qd, kd, vd, causal=w.causal, scale=w.scale, prefix=w.prefix,
-                                 alibi_slopes=sd)
-        return fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+                                 alibi_slopes=sd, **outs)
+        return fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, **outs)
     say("fa_fwd %s" % w.name)
     o, lse = call()
     o2, lse2 = call()
@@ -83,7 +96,8 @@ def test_varlen_full_size_sampled():
     cud = torch.from_numpy(cu).cuda()
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     say("fa_fwd_varlen %s" % w.name)
-    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, causal=True, scale=w.scale)
+    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, causal=True, scale=w.scale, out=nan_like(qd),
+                           lse=nan_like(qd, (w.H, qd.shape[0]), torch.float32))
     torch.cuda.synchronize()
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
     o_c, lse_c = o.cpu(), lse.cpu()
@@ -118,8 +132,10 @@ def test_decode_full_size_sampled():
         vc[b, L:min(w.Nk, L + 300)] = float("nan")
     sl = torch.from_numpy(lens.astype(np.int32)).cuda()
     say("fa_decode_splitkv %s" % w.name)
-    o, lse = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=w.chunk)
-    o2, lse2 = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=w.chunk)
+    qd = q.cuda()
+    dout = lambda: dict(out=nan_like(qd), lse=nan_like(qd, (w.B, w.H), torch.float32))
+    o, lse = fa.decode_splitkv(qd, kc, vc, sl, scale=w.scale, chunk=w.chunk, **dout())
+    o2, lse2 = fa.decode_splitkv(qd, kc, vc, sl, scale=w.scale, chunk=w.chunk, **dout())
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
     assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
@@ -164,9 +180,11 @@ def test_decode_paged_full_size_sampled():
     vp[bt.flatten().long()] = vc.view(-1, *pool[1:])
     sl = torch.from_numpy(lens.astype(np.int32)).cuda()
     say("fa_decode_splitkv_paged %s" % w.name)
-    o, lse = fa.decode_splitkv_paged(q.cuda(), kp, vp, sl, bt, scale=w.scale, chunk=w.chunk)
+    qd = q.cuda()
+    dout = lambda: dict(out=nan_like(qd), lse=nan_like(qd, (w.B, w.H), torch.float32))
+    o, lse = fa.decode_splitkv_paged(qd, kp, vp, sl, bt, scale=w.scale, chunk=w.chunk, **dout())
     say("fa_decode_splitkv (contiguous) %s" % w.name)
-    oc, lc = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=w.chunk)
+    oc, lc = fa.decode_splitkv(qd, kc, vc, sl, scale=w.scale, chunk=w.chunk, **dout())
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), oc.view(torch.int16)), "paged differs from contiguous"
     assert torch.equal(lse.view(torch.int32), lc.view(torch.int32))
@@ -196,9 +214,10 @@ def test_bwd_full_size_heads():
     do = wl.tensor(w, 3, (w.B, w.Nq, w.H, w.D))
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     say("fa_fwd + fa_bwd %s" % w.name)
-    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
-    g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)
-    g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=nan_like(qd),
+                    lse=nan_like(qd, (w.B, w.H, w.Nq), torch.float32))
+    g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, **nan_grads(qd, kd))
+    g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, **nan_grads(qd, kd))
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
@@ -224,11 +243,12 @@ def test_dropout_full_size_sampled():
     q, k, v = wl.prefill_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     say("fa_fwd_dropout %s" % w.name)
+    outs = lambda: dict(out=nan_like(qd), lse=nan_like(qd, (w.B, w.H, w.Nq), torch.float32))
     o, lse = fa.fwd_dropout(qd, kd, vd, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
-                            scale=w.scale)
+                            scale=w.scale, **outs())
     o2, lse2 = fa.fwd_dropout(qd, kd, vd, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
-                              scale=w.scale)
-    _, lse0 = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+                              scale=w.scale, **outs())
+    _, lse0 = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, **outs())
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
@@ -260,11 +280,12 @@ def test_dropout_bwd_full_size_heads():
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     say("fa_fwd_dropout + fa_bwd_dropout %s" % w.name)
     o, lse = fa.fwd_dropout(qd, kd, vd, dropout_p=w.dropout, seed=w.seed, causal=w.causal,
-                            scale=w.scale)
+                            scale=w.scale, out=nan_like(qd),
+                            lse=nan_like(qd, (w.B, w.H, w.Nq), torch.float32))
     g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dropout_p=w.dropout,
-                seed=w.seed)
+                seed=w.seed, **nan_grads(qd, kd))
     g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, dropout_p=w.dropout,
-                seed=w.seed)
+                seed=w.seed, **nan_grads(qd, kd))
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
@@ -304,8 +325,9 @@ def test_prefill_long_and_wide_sampled(case):
     q, k, v = wl.prefill_inputs(w)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     say("fa_fwd %s" % name)
-    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=w.scale)
-    o2, lse2 = fa.fwd(qd, kd, vd, causal=causal, scale=w.scale)
+    outs = lambda: dict(out=nan_like(qd), lse=nan_like(qd, (B, H, Nq), torch.float32))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=w.scale, **outs())
+    o2, lse2 = fa.fwd(qd, kd, vd, causal=causal, scale=w.scale, **outs())
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "run-to-run difference"
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
@@ -342,7 +364,9 @@ def test_decode_long_cache_sampled(chunk):
             vc[b, L:] = float("nan")
     sl = torch.from_numpy(lens.astype(np.int32)).cuda()
     say("fa_decode_splitkv Lk %s chunk %d" % (lens.tolist(), chunk))
-    o, lse = fa.decode_splitkv(q.cuda(), kc, vc, sl, scale=w.scale, chunk=chunk)
+    qd = q.cuda()
+    dout = lambda: dict(out=nan_like(qd), lse=nan_like(qd, (B, H), torch.float32))
+    o, lse = fa.decode_splitkv(qd, kc, vc, sl, scale=w.scale, chunk=chunk, **dout())
     ps = 64
     table = torch.arange(B * (Nk // ps), dtype=torch.int32, device="cuda").view(B, Nk // ps)
     table = table.flip(1).contiguous()  # pages in reverse pool order
@@ -350,8 +374,9 @@ def test_decode_long_cache_sampled(chunk):
     vp = torch.empty_like(kp)
     kp[table.flatten().long()] = kc.view(-1, ps, H, D)
     vp[table.flatten().long()] = vc.view(-1, ps, H, D)
-    op, lp = fa.decode_splitkv_paged(q.cuda(), kp, vp, sl, table, scale=w.scale, chunk=chunk)
+    op, lp = fa.decode_splitkv_paged(qd, kp, vp, sl, table, scale=w.scale, chunk=chunk, **dout())
     torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
     assert torch.equal(o.view(torch.int16), op.view(torch.int16)), "paged differs from contiguous"
     assert torch.equal(lse.view(torch.int32), lp.view(torch.int32))
     o_c, lse_c = o.cpu(), lse.cpu()
@@ -382,11 +407,12 @@ def test_bwd_masked_full_size_heads(cfg):
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
     say("fa_fwd_masked + fa_bwd_masked %s" % w.name)
     o, lse = fa.fwd_masked(qd, kd, vd, causal=w.causal, scale=w.scale, prefix=w.prefix,
-                           alibi_slopes=sd)
+                           alibi_slopes=sd, out=nan_like(qd),
+                           lse=nan_like(qd, (w.B, w.H, w.Nq), torch.float32))
     g1 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, prefix=w.prefix,
-                alibi_slopes=sd)
+                alibi_slopes=sd, **nan_grads(qd, kd))
     g2 = fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale, prefix=w.prefix,
-                alibi_slopes=sd)
+                alibi_slopes=sd, **nan_grads(qd, kd))
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
@@ -415,11 +441,12 @@ def test_bwd_varlen_full_size_sampled():
     lens = np.diff(cu)
     mx = int(lens.max())
     say("fa_fwd_varlen + fa_bwd_varlen %s" % w.name)
-    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, causal=True, scale=w.scale)
+    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, causal=True, scale=w.scale, out=nan_like(qd),
+                           lse=nan_like(qd, (w.H, qd.shape[0]), torch.float32))
     g1 = fa.bwd_varlen(qd, kd, vd, o, lse, dod, cud, cud, causal=True, scale=w.scale, max_seqlen_q=mx,
-                       max_seqlen_k=mx)
+                       max_seqlen_k=mx, **nan_grads(qd, kd))
     g2 = fa.bwd_varlen(qd, kd, vd, o, lse, dod, cud, cud, causal=True, scale=w.scale, max_seqlen_q=mx,
-                       max_seqlen_k=mx)
+                       max_seqlen_k=mx, **nan_grads(qd, kd))
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "run-to-run difference"
