@@ -25,6 +25,7 @@ from typing import Optional, Tuple
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16",
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
+    "FA_ERR_TOO_LARGE", "FA_NOALLOC_SCRATCH_BYTES", "fa_fwd_varlen_noalloc", "fwd_varlen_noalloc",
     "FaError", "library_path", "load",
     "fa_fwd", "fa_fwd_masked", "fa_fwd_dropout", "fa_bwd", "fa_bwd_masked", "fa_bwd_dropout",
     "fa_bwd_varlen", "fa_fwd_varlen_masked", "fa_fwd_varlen_dropout", "fa_bwd_varlen_masked",
@@ -37,6 +38,8 @@ __all__ = [
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_ERR_TOO_LARGE = 5
+FA_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
@@ -75,6 +78,8 @@ _SIGS = {
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                     _vp, _sz, _i, _vp]),
     "fa_fwd_varlen_workspace_bytes": (_sz, [_i, _i]),
+    "fa_fwd_varlen_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                   _i, _vp]),
     "fa_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp,
                            _sz, _i, _vp]),
     "fa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
@@ -242,6 +247,12 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, to
     return load().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q,
                                 total_k, H, D, scale, causal, workspace, workspace_bytes, dtype,
                                 stream)
+
+
+def fa_fwd_varlen_noalloc(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
+                          H, D, scale, causal, dtype, stream) -> int:
+    return load().fa_fwd_varlen_noalloc(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq,
+                                        total_q, total_k, H, D, scale, causal, dtype, stream)
 
 
 def fa_decode_workspace_bytes(B, H, Nk_max, D, chunk) -> int:
@@ -535,6 +546,28 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
     else:
         st = fa_fwd_varlen(*common, *tail)
         _check("fa_fwd_varlen", st)
+    return out, lse
+
+
+def fwd_varlen_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
+                       scale: Optional[float] = None, out=None, lse=None, return_lse: bool = True,
+                       stream=None) -> Tuple:
+    """fwd_varlen through fa_fwd_varlen_noalloc: the library allocates nothing (the tile
+    schedule lives in its static per-GPU scratch; calls that overlap on one GPU race).  Pass
+    out (and lse) to allocate nothing here either."""
+    import torch
+    total_q, H, D, total_k, nseq = _check_packed(q, k, v, cu_seqlens_q, cu_seqlens_k, None, out,
+                                                 lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    st = fa_fwd_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_k), nseq, total_q, total_k, H, D, float(scale),
+                               int(bool(causal)), _dtype_code(q), _stream(stream))
+    _check("fa_fwd_varlen_noalloc", st)
     return out, lse
 
 

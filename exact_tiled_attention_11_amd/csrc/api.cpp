@@ -119,7 +119,8 @@ fa_status_t fwd_varlen_impl(const void* q, const void* k, const void* v, void* o
                             int total_q, int total_k, int H, int D, float scale, int causal,
                             int prefix, const float* alibi_slopes, uint32_t drop_t,
                             float drop_scale, uint64_t seed, void* workspace,
-                            size_t workspace_bytes, fa_dtype_t dtype, void* stream);
+                            size_t workspace_bytes, fa_dtype_t dtype, void* stream,
+                            bool use_scratch = false);
 
 }  // namespace
 
@@ -132,6 +133,7 @@ const char* fa_status_string(fa_status_t s) {
     case FA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or chunk size";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_HIP: return "HIP error or no gfx950 device";
+    case FA_ERR_TOO_LARGE: return "problem exceeds the static scratch of the no-allocation call";
     default: return "unknown status";
   }
 }
@@ -462,7 +464,8 @@ fa_status_t fwd_varlen_impl(const void* q, const void* k, const void* v, void* o
                             int total_q, int total_k, int H, int D, float scale, int causal,
                             int prefix, const float* alibi_slopes, uint32_t drop_t,
                             float drop_scale, uint64_t seed, void* workspace,
-                            size_t workspace_bytes, fa_dtype_t dtype, void* stream) {
+                            size_t workspace_bytes, fa_dtype_t dtype, void* stream,
+                            bool use_scratch) {
   if (!dtype_ok(dtype) || (D != 64 && D != 128)) return FA_ERR_UNSUPPORTED;
   // the mask families and dropout are implemented by the 16-bit kernel only
   if (dtype == FA_F32 && (prefix != 0 || alibi_slopes || drop_t)) return FA_ERR_UNSUPPORTED;
@@ -480,11 +483,16 @@ fa_status_t fwd_varlen_impl(const void* q, const void* k, const void* v, void* o
   const long long max_tiles = fa::varlen_max_tiles(nseq, total_q, rows);
   if (max_tiles * H > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   const size_t need = fa::varlen_sched_bytes(nseq, max_tiles);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  } else if (!workspace || workspace_bytes < need) {
+    return FA_ERR_WORKSPACE;
+  }
 
   fa_status_t st = device_ok();
   if (st != FA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (use_scratch && fa::noalloc_scratch(&workspace) != hipSuccess) return FA_ERR_HIP;
 
   hipError_t e = fa::launch_varlen_schedule(cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
                                             rows, fa::fwd_key_tile(dtype, D), causal,
@@ -524,6 +532,16 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
                          D, scale, causal, 0, nullptr, 0u, 1.f, 0u, workspace, workspace_bytes,
                          dtype, stream);
+}
+
+fa_status_t fa_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                  int total_k, int H, int D, float scale, int causal,
+                                  fa_dtype_t dtype, void* stream) {
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, H,
+                         D, scale, causal, 0, nullptr, 0u, 1.f, 0u, nullptr, 0, dtype, stream,
+                         true);
 }
 
 fa_status_t fa_fwd_varlen_masked(const void* q, const void* k, const void* v, void* o,

@@ -49,6 +49,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -1197,6 +1198,31 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     sched[0] = min(scan[kSchedBins - 1], max_tiles);
     sched[1] = 0;
   }
+}
+
+// Schedule scratch of fa_fwd_varlen_noalloc.  In host code `scratch` names
+// a host-side stand-in, not device memory: its device address is looked up
+// once per device with that device current, and only that address is used.
+static __device__ __align__(256) int32_t scratch[FA_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev].store(p, std::memory_order_release);  // racing threads store the same address
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int nseq,

@@ -53,6 +53,10 @@ hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int 
                                   int causal, int max_tiles, int32_t* sched,
                                   hipStream_t stream);
 
+// Device address of the static schedule scratch of the current device
+// (FA_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
+
 // Upper bound on the number of (sequence, query block) tiles.
 inline long long varlen_max_tiles(int nseq, int total_q, int rows) {
   return ((long long)total_q + rows - 1) / rows + nseq;

@@ -68,7 +68,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1, /* null pointer, size out of range, misaligned pointer, non-finite scale */
   FA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, unsupported chunk size */
   FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes figure */
-  FA_ERR_HIP = 4          /* no usable gfx950 device, or a kernel launch failed */
+  FA_ERR_HIP = 4,         /* no usable gfx950 device, or a kernel launch failed */
+  FA_ERR_TOO_LARGE = 5    /* fa_fwd_varlen_noalloc: the schedule exceeds the static scratch */
 } fa_status_t;
 
 /*
@@ -130,6 +131,30 @@ FA355_API fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v,
                           int nseq, int total_q, int total_k, int H, int D, float scale,
                           int causal, void* workspace, size_t workspace_bytes,
                           fa_dtype_t dtype, void* stream);
+
+/*
+ * fa_fwd_varlen for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results, minus the workspace: the tile schedule goes to
+ * a static device array of FA_NOALLOC_SCRATCH_BYTES per GPU, which the
+ * library holds until the process ends.  The call allocates nothing.
+ *   Limit: the schedule, 4 * (2 + 4 * nseq + 2 * tiles) bytes rounded up to
+ *   256, with tiles = ceil(total_q / rows) + nseq and rows the query rows per
+ *   workgroup of the instance (fa_fwd_varlen_workspace_bytes(nseq, total_q)
+ *   is an upper bound), must fit: with 1 MiB that is, e.g., 1,000 sequences
+ *   of 16 million packed query rows.  Larger calls return FA_ERR_TOO_LARGE
+ *   before any HIP call.
+ *   The array keeps the last call's contents; the schedule kernel rewrites
+ *   every entry the forward reads, so nothing is cleared.  All calls on one
+ *   GPU share its array: calls that overlap on one GPU (other streams, other
+ *   threads) race and may compute wrong results.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (1u << 20)
+FA355_API fa_status_t fa_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* o,
+                                            float* lse, const int32_t* cu_seqlens_q,
+                                            const int32_t* cu_seqlens_k, int nseq, int total_q,
+                                            int total_k, int H, int D, float scale, int causal,
+                                            fa_dtype_t dtype, void* stream);
 
 /*
  * Single-token decode with the key/value cache split into chunks (split-KV).

@@ -30,7 +30,7 @@ def test_header_declares_the_api():
         "fa_bwd_varlen_masked", "fa_bwd_workspace_bytes", "fa_fwd_dropout",
         "fa_fwd", "fa_fwd_masked", "fa_fwd_varlen", "fa_fwd_varlen_dropout",
         "fa_fwd_varlen_masked", "fa_fwd_varlen_workspace_bytes", "fa_fwd_ex", "fa_bwd_ex",
-        "fa_fwd_varlen_ex", "fa_bwd_varlen_ex",
+        "fa_fwd_varlen_ex", "fa_bwd_varlen_ex", "fa_fwd_varlen_noalloc",
         "fa_decode_splitkv",
         "fa_decode_splitkv_paged", "fa_decode_workspace_bytes", "fa_status_string",
         "fa_version"])
@@ -44,8 +44,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
-        assert fa.fa_status_string(code)
+    for code in range(6):
+        assert fa.fa_status_string(code) != "unknown status"
     assert fa.fa_status_string(99) == "unknown status"
 
 
@@ -108,6 +108,30 @@ def test_varlen_validation():
     assert call(wsb=8) == fa.FA_ERR_WORKSPACE
     assert call(ws=MIS) == fa.FA_ERR_INVALID_ARG
     assert call(tq=0) == fa.FA_OK
+
+
+def test_varlen_noalloc_validation():
+    """The allocation-free call checks like fa_fwd_varlen, and rejects a schedule larger than its
+    static scratch with FA_ERR_TOO_LARGE, all before any HIP call."""
+    base = dict(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, nseq=2, tq=10, tk=10, H=2, D=128, scale=0.1,
+                causal=1, dtype=fa.FA_F16, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return fa.fa_fwd_varlen_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                        a["nseq"], a["tq"], a["tk"], a["H"], a["D"], a["scale"],
+                                        a["causal"], a["dtype"], a["stream"])
+    assert call(D=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(nseq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(cq=None) == fa.FA_ERR_INVALID_ARG
+    assert call(q=MIS) == fa.FA_ERR_INVALID_ARG
+    assert call(tq=0) == fa.FA_OK
+    # schedule bytes 4 * (2 + 4 nseq + 2 tiles) rounded to 256, tiles <= ceil(tq / 32) + nseq
+    assert call(nseq=70000, tq=70000) == fa.FA_ERR_TOO_LARGE       # 4 nseq alone is 1.1 MB
+    assert call(nseq=1, tq=1 << 30, tk=1 << 30) == fa.FA_ERR_TOO_LARGE
+    assert call(nseq=1, tq=1 << 30, tk=1 << 30, dtype=fa.FA_F32, D=64) == fa.FA_ERR_TOO_LARGE
+    assert fa.fa_status_string(fa.FA_ERR_TOO_LARGE).startswith("problem exceeds")
 
 
 def test_decode_validation():
