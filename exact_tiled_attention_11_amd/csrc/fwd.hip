@@ -921,11 +921,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     lrow += ts;
   };
 
-  // Block u.  First the exponents c*s - m of its scores (and, for a masked
-  // block, the mask: a hidden score becomes -2^109 or less; key 8*(r>>2) +
-  // 4*hh + (r&3) of the block is visible iff 8*(r>>2) + (r&3) <= lim, the
-  // bound added to each element's constant, which stays an instruction
-  // literal).  Then one chunk per MFMA (P V for block u-1, then the scores
+  // Block u.  First, for a masked block, the mask on its raw scores; then
+  // the exponents c*s - m of its scores.  Then one chunk per MFMA (P V for block u-1, then the scores
   // of block u+1); a chunk also issues the LDS read of a later MFMA and
   // takes its share of the exp2, add and pack work of the score pairs, so
   // the softmax's VALU work runs between MFMAs.  Scheduling fences keep the
@@ -934,6 +931,26 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
     if constexpr (DROP) keep_words_rows(kw, 2 * u, hh, wq0 + col, wi.h, wi.b, a.seed_lo, a.seed_hi);
+    // The mask, on the raw scores: a hidden one becomes -inf (exp2 gives 0 and
+    // it never wins a maximum).  Key 8*(e>>2) + 4*hh + (e&3) of the block is
+    // visible to query qi iff 8*(e>>2) + (e&3) <= lim.  Written in place: a
+    // select into new registers makes the compiler copy sS on the unmasked
+    // path of every block.
+    if (masked) {
+      const int qi = wq0 + col;
+      const int last = CAUSAL ? min(max(qi + off, pre), lk - 1) : lk - 1;
+      const int lim = last - u * C::kBC - 4 * hh;
+      const float ninf = -INFINITY;
+#define FA_HIDE(E)                                                         \
+  asm volatile("v_cmp_gt_i32 vcc, %2, %1\n\tv_cndmask_b32 %0, %0, %3, vcc" \
+               : "+v"(sS[E])                                               \
+               : "v"(lim), "n"(8 * ((E) >> 2) + ((E) & 3)), "v"(ninf)     \
+               : "vcc");
+      FA_HIDE(0) FA_HIDE(1) FA_HIDE(2) FA_HIDE(3) FA_HIDE(4) FA_HIDE(5) FA_HIDE(6) FA_HIDE(7)
+      FA_HIDE(8) FA_HIDE(9) FA_HIDE(10) FA_HIDE(11) FA_HIDE(12) FA_HIDE(13) FA_HIDE(14)
+      FA_HIDE(15)
+#undef FA_HIDE
+    }
     float addend = negm;
     // ALiBi: -slope * |key - position| in exp2 units, key 8*(r>>2) + 4*hh +
     // (r&3) of the block, position qi + off.  In a causal block left of the
@@ -961,16 +978,6 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
           const float d = dbase + (float)(8 * (r >> 2) + (r & 3));
           sX[r] = __builtin_fmaf(-slope2, fabsf(d), sX[r]);
         }
-      }
-    }
-    if (masked) {
-      const int qi = wq0 + col;
-      const int last = CAUSAL ? min(max(qi + off, pre), lk - 1) : lk - 1;
-      const float base = (float)(last - u * C::kBC - 4 * hh) * 0x1p110f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float cr = (float)(8 * (r >> 2) + (r & 3));
-        sX[r] = fminf(sX[r], base + (0.5f - cr) * 0x1p110f);
       }
     }
     frag op[NCH];  // LDS operand of MFMA i: P V (t-major) first, then the scores
