@@ -819,6 +819,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // the accumulators take
   int nwp = nw + 1;
   asm volatile("" : "+s"(nwp));
+  const int pq1 = nst >> 2, pq2 = nst >> 1, pq3 = nst - (nst >> 2);  // quarters of the blocks
   auto need_mask = [&](int u) __attribute__((always_inline)) {
     const int k0 = u * C::kBC;
     return (k0 + C::kBC > lk) || (CAUSAL && k0 + C::kBC - 1 > max(wq0 + off, pre));
@@ -1045,6 +1046,20 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     else if (loads_k) vm_wait<(PK - 1) * LPS>();
     else if (loads_v) vm_wait<PK * LPS>();
     __syncthreads();        // every wave's part is in; the slots of K u and V u-2 are free
+    // When every workgroup of the grid is resident at once (one round), the
+    // arbiter's oldest-wave-first order would finish the waves sharing a
+    // SIMD one after another and leave it to a single wave at the end; the
+    // priority of a wave falls instead with its work done (quarters of its
+    // blocks), so the waves of a SIMD progress together.  At head_dim 128 the
+    // priority is the MFMA chunks' (below).
+    if constexpr (D == 64) {
+      if (a.tail_prio) {
+        if (u < pq1) __builtin_amdgcn_s_setprio(3);
+        else if (u < pq2) __builtin_amdgcn_s_setprio(2);
+        else if (u < pq3) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    }
     issue(u, rc);
     // At u = nw every key of the block is hidden from this wave's rows (it
     // lies past the last one they see), so the masked form adds nothing but
@@ -1364,8 +1379,27 @@ int fwd_key_tile(fa_dtype_t dtype, int D) {
   }
 }
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype_t dtype, int D, bool causal, bool varlen,
+namespace {
+// Compute units of the current device, looked up once per device.
+constexpr int kCuDevices = 64;
+std::atomic<int> g_cus[kCuDevices];
+int cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int n = dev < kCuDevices ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < kCuDevices) g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& args, fa_dtype_t dtype, int D, bool causal, bool varlen,
                       unsigned grid, hipStream_t stream) {
+  FwdArgs a = args;
+  // the head_dim-64 pipelined kernel runs four workgroups per compute unit
+  a.tail_prio = dtype != FA_F32 && D == 64 && (long long)grid <= 4LL * cu_count();
   switch (dtype) {
     case FA_BF16:
       return D == 64 ? launch_t<__bf16, 64>(a, causal, varlen, grid, stream)

@@ -31,6 +31,9 @@ struct FwdArgs {
   uint32_t drop_t;         // a key is dropped when its random byte is below drop_t
   uint32_t seed_lo, seed_hi;
   float drop_scale;        // 256 / (256 - drop_t)
+  // set by the launcher: the whole grid is resident at once (one round of
+  // workgroups), so waves take priority by their remaining work
+  int tail_prio;
 };
 
 // Query rows per workgroup and keys per tile of the prefill kernel instance
