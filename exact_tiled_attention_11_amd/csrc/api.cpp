@@ -495,7 +495,7 @@ fa_status_t fwd_varlen_impl(const void* q, const void* k, const void* v, void* o
   if (use_scratch && fa::noalloc_scratch(&workspace) != hipSuccess) return FA_ERR_HIP;
 
   hipError_t e = fa::launch_varlen_schedule(cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k,
-                                            rows, fa::fwd_key_tile(dtype, D), causal,
+                                            rows, causal,
                                             (int)max_tiles, (int32_t*)workspace, s);
   if (e != hipSuccess) return FA_ERR_HIP;
   fa::FwdArgs a = {};

@@ -950,13 +950,7 @@ static hipError_t launch_bwd_td(const BwdArgs& a, bool causal, hipStream_t strea
   static_assert(kKB == kNW, "both dK/dV kernels cover 128 keys per workgroup");
   const unsigned gk = (unsigned)((a.Nk + kNW * kRows - 1) / (kNW * kRows)) * nbh;
   // head_dim 128: key blocks split over wave pairs (accumulators fit the VGPRs)
-#ifndef FA_BWD_SPLIT64
-#define FA_BWD_SPLIT64 0
-#endif
-#ifndef FA_BWD_SPLIT128
-#define FA_BWD_SPLIT128 1
-#endif
-  constexpr bool kSplit = D == 128 ? FA_BWD_SPLIT128 : FA_BWD_SPLIT64;
+  constexpr bool kSplit = D == 128;  // the split dK/dV kernel pays at head_dim 128 only
   const unsigned gq = (unsigned)a.nqb * nbh;
   const int mode = (a.drop_t ? kBwdDrop : 0) | (a.alibi ? kBwdAlibi : 0);
   auto launch2 = [&](auto mc, auto vc) {

@@ -313,13 +313,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   if (lane == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
 }
 
-#ifndef FA_DECODE_KPW
-#define FA_DECODE_KPW 64
-#endif
+constexpr int kDecodeKPW = 64;  // keys per wave of a chunk
 
 template <typename T, int D, int CHUNK, bool PAGED>
 static hipError_t launch_chunk(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int KPW = CHUNK < FA_DECODE_KPW ? CHUNK : FA_DECODE_KPW;  // keys per wave
+  constexpr int KPW = CHUNK < kDecodeKPW ? CHUNK : kDecodeKPW;  // keys per wave
   constexpr int NW = CHUNK / KPW;
   // One workgroup per work item: finished workgroups are replaced at once,
   // so the load phase of some overlaps the arithmetic of others.  (A

@@ -89,15 +89,13 @@ __device__ __forceinline__ bool any_mask(uint64_t m) {
 // workgroups, level 0 the longest.  The eight XCDs take workgroups in turn
 // (workgroup i goes to XCD i mod 8), each XCD with its own L2.  When the
 // (batch, head) pairs divide evenly over the XCDs, XCD x takes the pairs x,
-// x+8, ... in groups of FA_XCD_GROUP, one group after another, and within a
+// x+8, ... in groups of kXcdGroup, one group after another, and within a
 // group runs level by level over its pairs: an XCD then streams the K and V
 // (or Q and dO) of a few heads at a time, which stay in its L2 for the
 // workgroups that share them, while the longest blocks of a group still
 // start first.  Otherwise level l holds ids l*nbh .. l*nbh + nbh - 1.
-#ifndef FA_XCD_GROUP
-#define FA_XCD_GROUP 4
-#endif
-template <int G = FA_XCD_GROUP>
+constexpr int kXcdGroup = 4;
+template <int G = kXcdGroup>
 __device__ __forceinline__ void block_coords(int nbh, int& level, int& bh) {
   const int i = blockIdx.x;
   if (G > 0 && (nbh & 7) == 0) {

@@ -152,9 +152,8 @@ struct WorkItem {
   int b, h, qblk, lq, lk;
   long long q_tok0, k_tok0, lse_base;
 };
-#ifndef FA_XCD_GROUP_VARLEN
-#define FA_XCD_GROUP_VARLEN 1
-#endif
+// packed batches: each XCD walks the tile table one head at a time
+constexpr int kXcdGroupVarlen = 1;
 template <bool CAUSAL, bool VARLEN>
 __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
   if constexpr (!VARLEN) {
@@ -172,7 +171,7 @@ __device__ __forceinline__ bool work_item(const FwdArgs& a, WorkItem& w) {
     w.lse_base = ((long long)b * a.H + w.h) * a.Nq;
   } else {
     int t, h;
-    block_coords<FA_XCD_GROUP_VARLEN>(a.H, t, h);
+    block_coords<kXcdGroupVarlen>(a.H, t, h);
     w.h = h;
     if (t >= a.sched[0]) return false;
     const int* tl = a.sched + 2 + 4 * a.nseq + 2 * t;
@@ -634,17 +633,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 // the first of those zero loads fills the V slot of "block -1", whose
 // probabilities are zero too.
 // ---------------------------------------------------------------------------
-#ifndef FA_PIPE_LA
-#define FA_PIPE_LA 2  // LDS reads issued this many MFMAs ahead in the hot step
-#endif
+constexpr int kPipeLA = 2;  // LDS reads issued this many MFMAs ahead in the hot step
 // steps between a block's request and its first use: 2 at head_dim 64; 1 at
 // head_dim 128, whose steps are twice as long (3 % faster than 2 there)
-#ifndef FA_PIPE_PK64
-#define FA_PIPE_PK64 2
-#endif
-#ifndef FA_PIPE_PK128
-#define FA_PIPE_PK128 1
-#endif
+constexpr int kPipePK64 = 2, kPipePK128 = 1;
 
 template <typename T, int D, int NW, int PK>
 struct PipeCfg {
@@ -693,7 +685,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   constexpr int DB = D / 32;        // 32-wide blocks of head_dim
   constexpr int TS = 32 / E::kStep; // MFMA steps over a 32-key block (2)
   constexpr int RB = C::kCPR * 16;  // LDS bytes per block row
-  constexpr int LA = FA_PIPE_LA;
+  constexpr int LA = kPipeLA;
   constexpr int LPS = C::kLPS;
   constexpr int NPV = TS * DB;      // P V MFMAs per block
   constexpr int NCH = NPV + KS;     // MFMAs (chunks) per block
@@ -1109,32 +1101,17 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
 // Varlen schedule, written by one workgroup: the (sequence, query block)
 // tiles sequence by sequence, each sequence's longest first.  The forward
 // grid walks it per head on each XCD, so the workgroups an XCD runs at once
-// share the K and V of one or two sequences in its L2.  (FA_VARLEN_SEQ_MAJOR
-// 0: all tiles sorted by their number of key tiles, longest first, by a
-// counting sort over LDS bins.)
+// share the K and V of one or two sequences in its L2.
 // ---------------------------------------------------------------------------
-#ifndef FA_VARLEN_SEQ_MAJOR
-#define FA_VARLEN_SEQ_MAJOR 1
-#endif
 constexpr int kSchedThreads = 1024;
-constexpr int kSchedBins = 1024;
-
-__device__ __forceinline__ int tile_keys(int qb, int rows, int key_tile, int lq, int lk, int causal) {
-  const int all = (lk + key_tile - 1) / key_tile;
-  if (!causal) return all;
-  const int kmax = min((qb + 1) * rows, lq) - 1 + (lk - lq);
-  return kmax < 0 ? 0 : min(all, kmax / key_tile + 1);
-}
 
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
-    const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k, int rows,
-    int key_tile, int causal, int max_tiles, int* sched) {
-  __shared__ int hist[kSchedBins];
-  __shared__ int scan[kSchedBins];
+    const int* cu_q, const int* cu_k, int nseq, int total_q, int total_k, int rows, int causal,
+    int max_tiles, int* sched) {
+  __shared__ int part[kSchedThreads];
   const int tid = threadIdx.x;
   int* seq = sched + 2;
   int* tiles = sched + 2 + 4 * nseq;
-  for (int b = tid; b < kSchedBins; b += kSchedThreads) hist[b] = 0;
   // per-sequence bounds, clamped to the declared totals
   for (int s = tid; s < nseq; s += kSchedThreads) {
     const int q0 = min(max(cu_q[s], 0), total_q), q1 = min(max(cu_q[s + 1], q0), total_q);
@@ -1145,79 +1122,34 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     seq[4 * s + 3] = k1 - k0;
   }
   __syncthreads();
-  if constexpr (FA_VARLEN_SEQ_MAJOR) {
-    // the tiles of sequence 0, then of sequence 1, ...; within a sequence the
-    // longest first.  Offsets: an exclusive scan of the tile counts, taken
-    // kSchedThreads sequences at a time.
-    int* part = scan;
-    static_assert(kSchedBins == kSchedThreads, "the scan buffer holds one count per thread");
-    int carry = 0;  // tiles of the sequences before this chunk (the same in every thread)
-    for (int base = 0; base < nseq; base += kSchedThreads) {
-      const int s = base + tid;
-      const int n = s < nseq ? (seq[4 * s + 1] + rows - 1) / rows : 0;
-      part[tid] = n;
+  // the tiles of sequence 0, then of sequence 1, ...; within a sequence the
+  // longest first.  Offsets: an exclusive scan of the tile counts, taken
+  // kSchedThreads sequences at a time.
+  int carry = 0;  // tiles of the sequences before this chunk (the same in every thread)
+  for (int base = 0; base < nseq; base += kSchedThreads) {
+    const int s = base + tid;
+    const int n = s < nseq ? (seq[4 * s + 1] + rows - 1) / rows : 0;
+    part[tid] = n;
+    __syncthreads();
+    for (int st = 1; st < kSchedThreads; st <<= 1) {
+      const int v = tid >= st ? part[tid - st] : 0;
       __syncthreads();
-      for (int st = 1; st < kSchedThreads; st <<= 1) {
-        const int v = tid >= st ? part[tid - st] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-      }
-      const int first = carry + part[tid] - n;
-      for (int i = 0; i < n; ++i) {
-        const int pos = first + i;
-        if (pos < max_tiles) {
-          tiles[2 * pos] = s;
-          tiles[2 * pos + 1] = causal ? n - 1 - i : i;  // causal: the last query block sees the most keys
-        }
-      }
-      carry += part[kSchedThreads - 1];
-      __syncthreads();  // every thread has read part before the next chunk writes it
+      part[tid] += v;
+      __syncthreads();
     }
-    if (tid == 0) {
-      sched[0] = min(carry, max_tiles);
-      sched[1] = 0;
-    }
-    return;
-  }
-  for (int s = tid; s < nseq; s += kSchedThreads) {
-    const int lq = seq[4 * s + 1], lk = seq[4 * s + 3];
-    const int nqb = (lq + rows - 1) / rows;
-    for (int qb = 0; qb < nqb; ++qb)
-      atomicAdd(&hist[min(tile_keys(qb, rows, key_tile, lq, lk, causal), kSchedBins - 1)], 1);
-  }
-  __syncthreads();
-  // exclusive prefix over bins in descending order: start[b] = sum_{b' > b} hist[b']
-  for (int b = tid; b < kSchedBins; b += kSchedThreads) scan[b] = hist[kSchedBins - 1 - b];
-  __syncthreads();
-  for (int st = 1; st < kSchedBins; st <<= 1) {
-    int v = 0;
-    const int b = tid;
-    if (b < kSchedBins && b >= st) v = scan[b - st];
-    __syncthreads();
-    if (b < kSchedBins) scan[b] += v;
-    __syncthreads();
-  }
-  // scan[i] is now the inclusive sum of the i+1 largest bins
-  for (int b = tid; b < kSchedBins; b += kSchedThreads) {
-    const int i = kSchedBins - 1 - b;  // position of bin b in descending order
-    hist[b] = scan[i] - hist[b];       // start offset of bin b
-  }
-  __syncthreads();
-  for (int s = tid; s < nseq; s += kSchedThreads) {
-    const int lq = seq[4 * s + 1], lk = seq[4 * s + 3];
-    const int nqb = (lq + rows - 1) / rows;
-    for (int qb = 0; qb < nqb; ++qb) {
-      const int bin = min(tile_keys(qb, rows, key_tile, lq, lk, causal), kSchedBins - 1);
-      const int pos = atomicAdd(&hist[bin], 1);
+    const int first = carry + part[tid] - n;
+    for (int i = 0; i < n; ++i) {
+      const int pos = first + i;
       if (pos < max_tiles) {
         tiles[2 * pos] = s;
-        tiles[2 * pos + 1] = qb;
+        tiles[2 * pos + 1] = causal ? n - 1 - i : i;  // causal: the last query block sees the most keys
       }
     }
+    carry += part[kSchedThreads - 1];
+    __syncthreads();  // every thread has read part before the next chunk writes it
   }
   if (tid == 0) {
-    sched[0] = min(scan[kSchedBins - 1], max_tiles);
+    sched[0] = min(carry, max_tiles);
     sched[1] = 0;
   }
 }
@@ -1248,47 +1180,30 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int nseq,
-                                  int total_q, int total_k, int rows, int key_tile,
-                                  int causal, int max_tiles, int32_t* sched,
-                                  hipStream_t stream) {
+                                  int total_q, int total_k, int rows, int causal, int max_tiles,
+                                  int32_t* sched, hipStream_t stream) {
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_q,
-                     cu_k, nseq, total_q, total_k, rows, key_tile, causal, max_tiles, sched);
+                     cu_k, nseq, total_q, total_k, rows, causal, max_tiles, sched);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Instances and dispatch
 // ---------------------------------------------------------------------------
-// (QB, KB, NW, NBUF, OCC) per element type and head_dim: query blocks of 32
-// per wave, key blocks of 32 per tile, waves per workgroup, tiles in flight,
-// and the waves per SIMD the register budget is sized for.
-#ifndef FA_TILE_16_64
-#define FA_TILE_16_64 1, 2, 4, 2, 4
-#endif
-#ifndef FA_TILE_16_128
-#define FA_TILE_16_128 1, 2, 4, 2, 2
-#endif
+// fp32 tiles (QB, KB, NW, NBUF, OCC, KSPLIT): query blocks of 32 per wave,
+// key blocks of 32 per tile, waves per workgroup, tiles in flight, the waves
+// per SIMD the register budget is sized for, and the key split.
 template <int QB_, int KB_, int NW_, int NBUF_, int OCC_, int KSPLIT_ = 0>
 struct TileCfg {
   static constexpr int QB = QB_, KB = KB_, NW = NW_, NBUF = NBUF_, OCC = OCC_;
   static constexpr bool KSPLIT = KSPLIT_ != 0;
 };
 template <typename T, int D> struct Tile;
-template <> struct Tile<__bf16, 64> : TileCfg<FA_TILE_16_64> {};
-template <> struct Tile<_Float16, 64> : TileCfg<FA_TILE_16_64> {};
-template <> struct Tile<__bf16, 128> : TileCfg<FA_TILE_16_128> {};
-template <> struct Tile<_Float16, 128> : TileCfg<FA_TILE_16_128> {};
 // fp32 at head_dim 64: 32-row workgroups whose four waves split each
 // 128-key tile (the longest causal row block otherwise walks every key on
 // one wave: fp32 MFMAs are 16 times slower per flop than bf16 ones)
-#ifndef FA_TILE_32_64
-#define FA_TILE_32_64 1, 4, 4, 2, 2, 1
-#endif
-#ifndef FA_TILE_32_128
-#define FA_TILE_32_128 1, 1, 4, 2, 2
-#endif
-template <> struct Tile<float, 64> : TileCfg<FA_TILE_32_64> {};
-template <> struct Tile<float, 128> : TileCfg<FA_TILE_32_128> {};
+template <> struct Tile<float, 64> : TileCfg<1, 4, 4, 2, 2, 1> {};
+template <> struct Tile<float, 128> : TileCfg<1, 1, 4, 2, 2> {};
 
 template <typename K>
 static hipError_t launch_k(K kern, unsigned grid, int threads, int lds, hipStream_t stream,
@@ -1302,33 +1217,24 @@ static hipError_t launch_k(K kern, unsigned grid, int threads, int lds, hipStrea
   return hipGetLastError();
 }
 
-// 16-bit types take the software-pipelined kernel (same 128-row blocks as
-// Tile<., D>; its 32-key blocks fit the 64-key tiles the varlen schedule
-// counts, which only needs an upper bound).
-#ifndef FA_PIPE
-#define FA_PIPE 1
-#endif
+// 16-bit types take the software-pipelined kernel, fp32 the plain tiled one.
 template <typename T, int D>
 struct UsePipe {
-  static constexpr bool value = FA_PIPE && sizeof(T) == 2;
+  static constexpr bool value = sizeof(T) == 2;
 };
-#ifndef FA_PIPE_NW64
-#define FA_PIPE_NW64 4
-#endif
-#ifndef FA_PIPE_NW128
-#define FA_PIPE_NW128 4
-#endif
-// waves (of 32 query rows each) per workgroup of the pipelined kernel
+// waves (of 32 query rows each) per workgroup of the pipelined kernel (eight
+// at head_dim 64 halve the K/V traffic into LDS, and the power drawn, but
+// couple two waves of a SIMD through the barrier: no faster)
 template <int D>
 struct PipeNW {
-  static constexpr int value = D == 64 ? FA_PIPE_NW64 : FA_PIPE_NW128;
+  static constexpr int value = 4;
 };
 
 template <typename T, int D>
 static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned grid,
                            hipStream_t stream) {
   if constexpr (UsePipe<T, D>::value) {
-    constexpr int NW = PipeNW<D>::value, PK = D == 128 ? FA_PIPE_PK128 : FA_PIPE_PK64;
+    constexpr int NW = PipeNW<D>::value, PK = D == 128 ? kPipePK128 : kPipePK64;
     constexpr int lds = PipeCfg<T, D, NW, PK>::kLdsB;
     // one instance per (mode, causal, packed)
     auto go = [&](auto mc) {
@@ -1344,38 +1250,30 @@ static hipError_t launch_t(const FwdArgs& a, bool causal, bool varlen, unsigned 
     if (a.alibi) return go(IC<kPipeAlibi>{});
     if (a.drop_t) return go(IC<kPipeDrop>{});
     return go(IC<kPipePlain>{});
+  } else {
+    using Tl = Tile<T, D>;
+    constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;
+    constexpr bool KSP = Tl::KSPLIT;
+    constexpr int lds = FwdCfg<T, D, QB, KB, NW, NB, KSP>::kLdsB;
+    if (causal) {
+      if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, true, true>, grid, NW * 64, lds, stream, a);
+      return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, true, false>, grid, NW * 64, lds, stream, a);
+    }
+    if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, false, true>, grid, NW * 64, lds, stream, a);
+    return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, false, false>, grid, NW * 64, lds, stream, a);
   }
-  using Tl = Tile<T, D>;
-  constexpr int QB = Tl::QB, KB = Tl::KB, NW = Tl::NW, NB = Tl::NBUF, OC = Tl::OCC;
-  constexpr bool KSP = Tl::KSPLIT;
-  constexpr int lds = FwdCfg<T, D, QB, KB, NW, NB, KSP>::kLdsB;
-  if (causal) {
-    if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, true, true>, grid, NW * 64, lds, stream, a);
-    return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, true, false>, grid, NW * 64, lds, stream, a);
-  }
-  if (varlen) return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, false, true>, grid, NW * 64, lds, stream, a);
-  return launch_k(fwd_kernel<T, D, QB, KB, NW, NB, OC, KSP, false, false>, grid, NW * 64, lds, stream, a);
 }
 
 template <typename T, int D> static int rows_t() {
   if constexpr (UsePipe<T, D>::value) return PipeNW<D>::value * 32;
-  return (Tile<T, D>::KSPLIT ? 1 : Tile<T, D>::NW) * 32 * Tile<T, D>::QB;
+  else return (Tile<T, D>::KSPLIT ? 1 : Tile<T, D>::NW) * 32 * Tile<T, D>::QB;
 }
-template <typename T, int D> static int keys_t() { return 32 * Tile<T, D>::KB; }
 
 int fwd_block_rows(fa_dtype_t dtype, int D) {
   switch (dtype) {
     case FA_BF16: return D == 64 ? rows_t<__bf16, 64>() : rows_t<__bf16, 128>();
     case FA_F16: return D == 64 ? rows_t<_Float16, 64>() : rows_t<_Float16, 128>();
     default: return D == 64 ? rows_t<float, 64>() : rows_t<float, 128>();
-  }
-}
-
-int fwd_key_tile(fa_dtype_t dtype, int D) {
-  switch (dtype) {
-    case FA_BF16: return D == 64 ? keys_t<__bf16, 64>() : keys_t<__bf16, 128>();
-    case FA_F16: return D == 64 ? keys_t<_Float16, 64>() : keys_t<_Float16, 128>();
-    default: return D == 64 ? keys_t<float, 64>() : keys_t<float, 128>();
   }
 }
 

@@ -36,10 +36,8 @@ struct FwdArgs {
   int tail_prio;
 };
 
-// Query rows per workgroup and keys per tile of the prefill kernel instance
-// chosen for (dtype, D).
+// Query rows per workgroup of the prefill kernel instance chosen for (dtype, D).
 int fwd_block_rows(fa_dtype_t dtype, int D);
-int fwd_key_tile(fa_dtype_t dtype, int D);
 
 // Fixed-length grid: B * H * ceil(Nq / rows); varlen grid: H * max_tiles.
 hipError_t launch_fwd(const FwdArgs& a, fa_dtype_t dtype, int D, bool causal, bool varlen,
@@ -52,9 +50,8 @@ hipError_t launch_fwd(const FwdArgs& a, fa_dtype_t dtype, int D, bool causal, bo
 //   sched[2 + 4*nseq + 2t]   tile t: sequence, query block; tiles sequence by
 //                            sequence, each sequence's longest first
 hipError_t launch_varlen_schedule(const int32_t* cu_q, const int32_t* cu_k, int nseq,
-                                  int total_q, int total_k, int rows, int key_tile,
-                                  int causal, int max_tiles, int32_t* sched,
-                                  hipStream_t stream);
+                                  int total_q, int total_k, int rows, int causal, int max_tiles,
+                                  int32_t* sched, hipStream_t stream);
 
 // Device address of the static schedule scratch of the current device
 // (FA_NOALLOC_SCRATCH_BYTES bytes), looked up once per device.

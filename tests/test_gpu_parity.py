@@ -153,6 +153,17 @@ VARLEN = [
     # runs over three chunks of sequences, some of them empty
     dataclasses.replace(wl.SMALL[4], name="varlen 2500 short sequences", dtype="bf16", D=64, H=2,
                         nseq=2500, len_lo=0, len_hi=40, seed=14),
+    # head counts divisible by 8 take the XCD-grouped order of the packed grid
+    dataclasses.replace(wl.SMALL[4], name="varlen causal bf16 D64 H8 5 seqs", dtype="bf16", D=64,
+                        H=8, nseq=5, len_lo=1, len_hi=400, seed=15),
+    dataclasses.replace(wl.SMALL[4], name="varlen noncausal f16 D128 H16 4 seqs", dtype="f16",
+                        D=128, H=16, causal=False, nseq=4, len_lo=1, len_hi=300, seed=16),
+    dataclasses.replace(wl.SMALL[4], name="varlen causal f16 D128 H16 3 seqs", dtype="f16",
+                        D=128, H=16, nseq=3, len_lo=100, len_hi=500, seed=17),
+    dataclasses.replace(wl.SMALL[4], name="varlen noncausal bf16 D64 H8 6 seqs", dtype="bf16",
+                        D=64, H=8, causal=False, nseq=6, len_lo=0, len_hi=350, seed=18),
+    dataclasses.replace(wl.SMALL[4], name="varlen 1100 short sequences H8", dtype="bf16", D=64,
+                        H=8, nseq=1100, len_lo=0, len_hi=40, seed=19),
 ]
 
 
