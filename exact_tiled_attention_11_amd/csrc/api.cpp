@@ -167,10 +167,15 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                        dtype, stream);
 }
 
-size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
-  if (B < 1 || H < 1 || Nq < 0) return 0;
+// Half of the gradient workspace: one float per (batch, head, query row).
+static size_t bwd_half_bytes(int B, int H, int Nq) {
   const size_t n = (size_t)B * H * (Nq > 0 ? Nq : 1);
   return (n * 4 + 255) / 256 * 256;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Nq) {
+  if (B < 1 || H < 1 || Nq < 0) return 0;
+  return 2 * bwd_half_bytes(B, H, Nq);  // rowsum(dO o O), then lse in exp2 units
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -247,6 +252,7 @@ fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
   a.dout = dout;
   a.lse = lse;
   a.delta = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + bwd_half_bytes(B, H, Nq));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -321,6 +327,7 @@ fa_status_t bwd_varlen_impl(const void* q, const void* k, const void* v, const v
   a.dout = dout;
   a.lse = lse;
   a.delta = (float*)workspace;
+  a.lse2 = (float*)((char*)workspace + bwd_half_bytes(1, H, total_q));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

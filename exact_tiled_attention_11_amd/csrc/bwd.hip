@@ -217,7 +217,8 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO o O) for every (query row, head), in lse's layout
+// delta = rowsum(dO o O) and lse2 = lse * log2 e for every (query row, head),
+// in lse's layout
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -231,13 +232,19 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 8; ++c) s += dot8_16<T>(po[c], pd[c]);
+  long long idx;
   if constexpr (VARLEN) {
-    a.delta[(long long)h * a.total_q + tok] = s;
+    idx = (long long)h * a.total_q + tok;
   } else {
     const int i = (int)(tok % a.Nq);
     const int b = (int)(tok / a.Nq);
-    a.delta[((long long)b * a.H + h) * a.Nq + i] = s;
+    idx = ((long long)b * a.H + h) * a.Nq + i;
   }
+  a.delta[idx] = s;
+  // the row's exp2 offset for the gradient kernels: probabilities are
+  // exp2(c s - lse2); +inf for a row with no visible key (probability 0)
+  const float l = a.lse[idx];
+  a.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
 }
 
 // ---------------------------------------------------------------------------
@@ -298,11 +305,15 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
   constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
-  using TP = TilePair<T, D>;
   constexpr int KS = D / 16, DB = D / 32, TS = 2, RB = D * 2;
-  constexpr int kBufB = 2 * TP::kTileB + 2 * kRows * 4;  // Q, dO, lse, delta
+  constexpr int kTileB = kRows * RB;                     // one 32-row tile
+  constexpr int kBufB = 2 * kTileB + 2 * kRows * 4;      // a stage: Q, dO, lse2, delta
+  constexpr int kStages = 3;                              // chunks c (read), c+1, c+2 (landing)
+  constexpr int kCPR = D / 8;                            // 16-byte chunks per row
+  constexpr int kLPT = kRows * kCPR / (kNW * 64);        // 16-byte loads per lane per tile
+  static_assert(kLPT >= 1 && kRows * kCPR % (kNW * 64) == 0, "a tile divides evenly over the lanes");
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kBufB];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kStages * kBufB];
   FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
   __shared__ __attribute__((aligned(16))) char trbuf_raw[DROP ? kNW * kTrWave : 16];
 
@@ -323,7 +334,6 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
   const size_t rs = (size_t)a.H * D;
   const T* qb = (const T*)a.q + (size_t)wi.q_tok0 * rs + (size_t)h * D;
   const T* dob = (const T*)a.dout + (size_t)wi.q_tok0 * rs + (size_t)h * D;
-  const float* lseb = a.lse + wi.stat0;
   const float* dlb = a.delta + wi.stat0;
 
   // K and V rows of this lane's key (B operands), zero past the real keys
@@ -339,6 +349,7 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
       vf[ks] = ok ? *(const frag*)(vr + ks * 16 + hh * 8) : z;
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // K and V complete before any tile load is counted
   f32x16_t dka[DB], dva[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16_t{};
@@ -357,33 +368,48 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 
   ReadLanes<D> rl;
   rl.init(lane);
-  TP st;
-  float st_l = 0.f;  // thread < 64: one lse (tid < 32) or delta (32 <= tid < 64) value
-  auto stage_load = [&](int c) {
-    st.load(qb, dob, rs, c * kRows, lq, tid);
-    if (tid < 2 * kRows) {
-      const int i = c * kRows + (tid & 31);
-      if (tid < kRows) {
-        // exp2 offset of row i; +inf for rows past the end or with no visible
-        // key (their probabilities are 0)
-        const float l = i < lq ? lseb[i] : -INFINITY;
-        st_l = l == -INFINITY ? INFINITY : l * kLog2e;
-      } else {
-        st_l = i < lq ? dlb[i] : 0.f;
-      }
+  // Stage of chunk c (32 query rows): Q and dO rows reach LDS through direct
+  // buffer loads (rows past the end are outside the buffer range and arrive
+  // as zeros), with the XOR swizzle applied on the global side; wave 0 also
+  // loads the rows' lse2 (lanes 0-31) and delta (lanes 32-63), zero past the
+  // end (such rows then have P = 1 but dO = 0 and delta = 0: they add
+  // nothing to dV or dK).
+  unsigned voff[kLPT];
+#pragma unroll
+  for (int l = 0; l < kLPT; ++l) {
+    const int p = (l * kNW + wave) * 64 + lane;  // 16-byte position within the tile
+    const int r = p / kCPR, pos = p % kCPR;
+    voff[l] = (unsigned)r * (unsigned)(rs * sizeof(T)) + (unsigned)((pos ^ bswz(r)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(size_t)smem;
+  const unsigned rsb = (unsigned)(rs * sizeof(T));
+  auto issue = [&](int c) {
+    const int rows = max(0, min(kRows, lq - c * kRows));
+    const unsigned sb = lds0 + (c % kStages) * kBufB;
+    const u32x4_t rq = make_rsrc((const char*)(qb + (size_t)c * kRows * rs), (unsigned)rows * rsb);
+    const u32x4_t rd = make_rsrc((const char*)(dob + (size_t)c * kRows * rs), (unsigned)rows * rsb);
+#pragma unroll
+    for (int l = 0; l < kLPT; ++l) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (l * kNW + wave) * 1024);
+      dma16(rq, voff[l], m0);
+      dma16(rd, voff[l], m0 + kTileB);
     }
-  };
-  auto stage_store = [&](int buf) {
-    FA_LDS(char)* base = smem + buf * kBufB;
-    st.store(base, base + TP::kTileB, tid);
-    if (tid < 2 * kRows) *(FA_LDS(float)*)(base + 2 * TP::kTileB + tid * 4) = st_l;
+    if (wave == 0) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + 2 * kTileB);
+      if (lane < kRows)
+        dma4(make_rsrc((const char*)(a.lse2 + wi.stat0 + c * kRows), (unsigned)rows * 4),
+             (unsigned)lane * 4, m0);
+      else
+        dma4(make_rsrc((const char*)(dlb + c * kRows), (unsigned)rows * 4),
+             (unsigned)(lane - kRows) * 4, m0);
+    }
   };
 
   auto compute = [&](int c, int buf) {
     const FA_LDS(char)* base = smem + buf * kBufB;
     const FA_LDS(char)* tq = base;
-    const FA_LDS(char)* tdo = base + TP::kTileB;
-    const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * TP::kTileB);
+    const FA_LDS(char)* tdo = base + kTileB;
+    const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * kTileB);
     const int q0 = c * kRows;
     // S = Q K^T and dP = dO V^T: rows (queries) along registers, lanes = keys
     f32x16_t s = {}, dp = {};
@@ -447,18 +473,21 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
       }
   };
 
-  if (c_begin < nch) {
-    stage_load(c_begin);
-    stage_store(0);
-  }
-  __syncthreads();
-  if (c_begin + 1 < nch) stage_load(c_begin + 1);
+  if (c_begin < nch) issue(c_begin);
+  if (c_begin + 1 < nch) issue(c_begin + 1);
   for (int c = c_begin; c < nch; ++c) {
-    const int buf = (c - c_begin) & 1;
-    if (wave_live && c >= c_wave) compute(c, buf);
-    if (c + 1 < nch) stage_store(buf ^ 1);  // its last reader was step c-1
-    __syncthreads();
-    if (c + 2 < nch) stage_load(c + 2);
+    // this wave's part of chunk c is in once at most the next chunk's loads
+    // are pending (wave 0 also issues the two statistics loads, each with
+    // half of its lanes)
+    if (c + 1 < nch) {
+      if (wave == 0) vm_wait<2 * kLPT + 2>();
+      else vm_wait<2 * kLPT>();
+    } else {
+      vm_wait<0>();
+    }
+    __syncthreads();  // every part of chunk c is in; every wave is done with chunk c-1's stage
+    if (c + 2 < nch) issue(c + 2);
+    if (wave_live && c >= c_wave) compute(c, c % kStages);
   }
 
   // dK = scale * dK^T, dV = dV^T (times 1 / (1 - p) with dropout) for keys
@@ -760,11 +789,15 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
   constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
-  using TP = TilePair<T, D>;
   constexpr int KS = D / 16, DB = D / 32, TS = 2, RB = D * 2;
-  constexpr int kBufB = 2 * TP::kTileB;  // K, V
+  constexpr int kTileB = kRows * RB;                     // one 32-row tile
+  constexpr int kBufB = 2 * kTileB;                      // a stage: K, V
+  constexpr int kStages = 3;                              // blocks j (read), j+1, j+2 (landing)
+  constexpr int kCPR = D / 8;                            // 16-byte chunks per row
+  constexpr int kLPT = kRows * kCPR / (kNW * 64);        // 16-byte loads per lane per tile
+  static_assert(kLPT >= 1 && kRows * kCPR % (kNW * 64) == 0, "a tile divides evenly over the lanes");
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * kBufB];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kStages * kBufB];
   FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 31, hh = lane >> 5;
@@ -798,11 +831,11 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
       dof[ks] = ok ? *(const frag*)((const T*)a.dout + ro + ks * 16 + hh * 8) : z;
     }
     if (ok) {
-      const float l = a.lse[wi.stat0 + qi];
-      lrow = l == -INFINITY ? INFINITY : l * kLog2e;
+      lrow = a.lse2[wi.stat0 + qi];
       drow = a.delta[wi.stat0 + qi];
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // Q, dO and the row statistics complete before any tile load
   f32x16_t dqa[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16_t{};
@@ -823,10 +856,32 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
 
   ReadLanes<D> rl;
   rl.init(lane);
-  TP st;
+  // Stage of key block j: K and V rows through direct buffer loads (rows
+  // past the end arrive as zeros), swizzled on the global side.
+  const unsigned rsb = (unsigned)(rs * sizeof(T));
+  unsigned voff[kLPT];
+#pragma unroll
+  for (int l = 0; l < kLPT; ++l) {
+    const int p = (l * kNW + wave) * 64 + lane;
+    const int r = p / kCPR, pos = p % kCPR;
+    voff[l] = (unsigned)r * rsb + (unsigned)((pos ^ bswz(r)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(size_t)(FA_LDS(char)*)smem_raw;
+  auto issue = [&](int j) {
+    const int rows = max(0, min(kRows, lk - j * kRows));
+    const unsigned sb = lds0 + (j % kStages) * kBufB;
+    const u32x4_t rk = make_rsrc((const char*)(kb + (size_t)j * kRows * rs), (unsigned)rows * rsb);
+    const u32x4_t rv = make_rsrc((const char*)(vb + (size_t)j * kRows * rs), (unsigned)rows * rsb);
+#pragma unroll
+    for (int l = 0; l < kLPT; ++l) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (l * kNW + wave) * 1024);
+      dma16(rk, voff[l], m0);
+      dma16(rv, voff[l], m0 + kTileB);
+    }
+  };
   auto compute = [&](int j, int buf) {
     const FA_LDS(char)* tk = smem + buf * kBufB;
-    const FA_LDS(char)* tv = tk + TP::kTileB;
+    const FA_LDS(char)* tv = tk + kTileB;
     const int k0 = j * kRows;
     // S^T = K Q^T and dP^T = V dO^T: keys along registers, lanes = queries
     f32x16_t s = {}, dp = {};
@@ -898,21 +953,15 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
     }
   };
 
-  if (nkb > 0) {
-    st.load(kb, vb, rs, 0, lk, tid);
-    st.store(smem, smem + TP::kTileB, tid);
-  }
-  __syncthreads();
-  if (1 < nkb) st.load(kb, vb, rs, kRows, lk, tid);
+  if (nkb > 0) issue(0);
+  if (1 < nkb) issue(1);
   for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
-    if (j < nkw) compute(j, buf);
-    if (j + 1 < nkb) {
-      FA_LDS(char)* nb = smem + (buf ^ 1) * kBufB;  // its last reader was step j-1
-      st.store(nb, nb + TP::kTileB, tid);
-    }
-    __syncthreads();
-    if (j + 2 < nkb) st.load(kb, vb, rs, (j + 2) * kRows, lk, tid);
+    // this wave's part of block j is in once at most the next block's loads are pending
+    if (j + 1 < nkb) vm_wait<2 * kLPT>();
+    else vm_wait<0>();
+    __syncthreads();  // every part of block j is in; every wave is done with block j-1's stage
+    if (j + 2 < nkb) issue(j + 2);
+    if (j < nkw) compute(j, j % kStages);
   }
 
   if (qi < lq) {

@@ -113,6 +113,37 @@ __device__ __forceinline__ void block_coords(int nbh, int& level, int& bh) {
   }
 }
 
+// One 16-byte direct-to-LDS load per lane: LDS[m0 + 16*lane] <- buffer[voff].
+// Written as inline assembly because the compiler's own form makes every
+// later LDS read wait for all such loads; the kernels count them themselves.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc, unsigned voff, unsigned m0) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+
+// The same for 4 bytes per lane: LDS[m0 + 4*lane] <- buffer[voff].
+__device__ __forceinline__ void dma4(const u32x4_t& rsrc, unsigned voff, unsigned m0) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Buffer resource for `bytes` bytes from `base` (raw, stride 0: offsets at or
+// beyond `bytes` read as zero).
+__device__ __forceinline__ u32x4_t make_rsrc(const char* base, unsigned bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

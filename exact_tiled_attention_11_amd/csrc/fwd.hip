@@ -119,30 +119,6 @@ __device__ __forceinline__ int swz_v(int r) {
                   : (((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r ^ (r >> 2)) & 1) << 3));
 }
 
-// One 16-byte direct-to-LDS load per lane: LDS[m0 + 16*lane] <- buffer[voff].
-// Written as inline assembly because the compiler's own form makes every
-// later LDS read wait for all such loads; this kernel counts them itself.
-__device__ __forceinline__ void dma16(const u32x4_t& rsrc, unsigned voff, unsigned m0) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Buffer resource for `bytes` bytes from `base` (raw, stride 0: offsets at or
-// beyond `bytes` read as zero).
-__device__ __forceinline__ u32x4_t make_rsrc(const char* base, unsigned bytes) {
-  const unsigned long long p = (unsigned long long)base;
-  u32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
-  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000u;
-  return r;
-}
 
 // The (sequence, head, query block) a workgroup computes.  Fixed-length
 // grids take query blocks as levels with (batch, head) fastest, causal ones

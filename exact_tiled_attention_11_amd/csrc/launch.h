@@ -92,6 +92,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;        // [B, H, Nq]
   float* delta;            // workspace [B, H, Nq]: rowsum(dO * O)
+  float* lse2;             // workspace, delta's layout: lse * log2 e (+inf: no visible key)
   void* dq;
   void* dk;
   void* dv;

@@ -219,7 +219,8 @@ FA355_API fa_status_t fa_decode_splitkv_paged(const void* q, const void* k_pages
  *   lse: [B, H, Nq] float32 from fa_fwd (rows with no visible key: -inf)
  *   seqlens_k: as fa_fwd; padding keys (rows Lk .. Nk-1) get dk = dv = 0
  *   workspace: device buffer of at least fa_bwd_workspace_bytes(B, H, Nq)
- *       bytes (rowsum(dO o O), float32); contents on entry do not matter
+ *       bytes (per query row rowsum(dO o O) and lse in base-2 units, float32);
+ *       contents on entry do not matter
  * Three kernel launches on `stream` (row sums, then dK/dV, then dQ); no
  * atomics, so the result is bit-reproducible.  The caller owns every buffer.
  */

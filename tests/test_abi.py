@@ -225,7 +225,7 @@ def test_bwd_validation():
         return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
                          a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"], a["scale"],
                          a["causal"], a["sl"], a["ws"], a["wsb"], a["dtype"], a["stream"])
-    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 2560          # 600 floats, 256-byte rounded
+    assert fa.fa_bwd_workspace_bytes(2, 3, 100) == 5120          # 2 x 600 floats, each 256-byte rounded
     assert fa.fa_bwd_workspace_bytes(0, 3, 100) == 0
     assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED        # 16-bit only
     assert call(D=96) == fa.FA_ERR_UNSUPPORTED
