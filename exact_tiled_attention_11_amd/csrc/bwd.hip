@@ -77,66 +77,6 @@ __device__ __forceinline__ float dot8_16(const u32x4_t& x, const u32x4_t& y) {
   return s;
 }
 
-// Two 32-row tiles (rows x D) staged global -> VGPRs -> LDS by the whole
-// workgroup of NT threads: each thread moves kPer 16-byte chunks of each
-// tile, or, when the two tiles hold one chunk per thread, one chunk of one
-// of them.
-template <typename T, int D, int NT = kNW * 64>
-struct TilePair {
-  static constexpr int kCPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int kRB = D * 2;                  // bytes per row
-  static constexpr int kTileB = kRows * kRB;
-  static constexpr int kChunks = kRows * kCPR;       // chunks per tile
-  static constexpr bool kOne = 2 * kChunks == NT;    // one chunk per thread in all
-  static constexpr int kPer = kOne ? 1 : kChunks / NT;  // chunks per thread per tile
-  static_assert(kOne || (kPer >= 1 && kPer * NT == kChunks), "whole chunks per thread");
-  u32x4_t a[kPer], b[kOne ? 1 : kPer];
-
-  // rows row0 .. row0+31 of the two tensors (token stride rs elements),
-  // rows >= nrows read as zero
-  __device__ __forceinline__ void load(const T* pa, const T* pb, size_t rs, int row0, int nrows,
-                                       int tid) {
-    if constexpr (kOne) {
-      const int p = tid % kChunks;
-      const int r = p / kCPR, c = p % kCPR;
-      const int row = row0 + r;
-      const T* src = tid < kChunks ? pa : pb;
-      a[0] = row < nrows ? *(const u32x4_t*)(src + (size_t)row * rs + c * 8) : u32x4_t{};
-    } else {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int p = tid + u * NT;
-        const int r = p / kCPR, c = p % kCPR;
-        const int row = row0 + r;
-        if (row < nrows) {
-          a[u] = *(const u32x4_t*)(pa + (size_t)row * rs + c * 8);
-          b[u] = *(const u32x4_t*)(pb + (size_t)row * rs + c * 8);
-        } else {
-          a[u] = u32x4_t{};
-          b[u] = u32x4_t{};
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store(FA_LDS(char)* ta, FA_LDS(char)* tb, int tid) const {
-    if constexpr (kOne) {
-      const int p = tid % kChunks;
-      const int r = p / kCPR, c = p % kCPR;
-      const int pos = r * kRB + ((c ^ bswz(r)) * 16);
-      *(FA_LDS(u32x4_t)*)((tid < kChunks ? ta : tb) + pos) = a[0];
-    } else {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int p = tid + u * NT;
-        const int r = p / kCPR, c = p % kCPR;
-        const int pos = r * kRB + ((c ^ bswz(r)) * 16);
-        *(FA_LDS(u32x4_t)*)(ta + pos) = a[u];
-        *(FA_LDS(u32x4_t)*)(tb + pos) = b[u];
-      }
-    }
-  }
-};
-
 // Lane parts of the two LDS read patterns of a 32-row tile.
 template <int D>
 struct ReadLanes {
@@ -536,11 +476,15 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
   constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
-  using TP = TilePair<T, D, kSplitNW * 64>;
   constexpr int KS = D / 16, DB = D / 32, TS = 2, RB = D * 2;
-  constexpr int kBufB = 2 * TP::kTileB + 2 * kRows * 4;  // Q, dO, lse, delta
+  constexpr int kTileB = kRows * RB;                     // one 32-row tile
+  constexpr int kBufB = 2 * kTileB + 2 * kRows * 4;      // a stage: Q, dO, lse2, delta
   typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-  constexpr int kStages = 3;  // chunk c - 1 (dS waves), c (P waves), c + 1 (staged)
+  // chunk c - 1 (dS waves), c (both), c + 1 and c + 2 (landing)
+  constexpr int kStages = 4;
+  constexpr int kCPR = D / 8;                            // 16-byte chunks per row
+  constexpr int kLPT = kRows * kCPR / (kSplitNW * 64);   // 16-byte loads per lane per tile
+  static_assert(kLPT >= 1 && kRows * kCPR % (kSplitNW * 64) == 0, "a tile divides evenly over the lanes");
 
   __shared__ __attribute__((aligned(16))) char smem_raw[kStages * kBufB];
   FA_LDS(char)* smem = (FA_LDS(char)*)smem_raw;
@@ -569,7 +513,6 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
   const size_t rs = (size_t)a.H * D;
   const T* qb = (const T*)a.q + (size_t)wi.q_tok0 * rs + (size_t)h * D;
   const T* dob = (const T*)a.dout + (size_t)wi.q_tok0 * rs + (size_t)h * D;
-  const float* lseb = a.lse + wi.stat0;
   const float* dlb = a.delta + wi.stat0;
 
   // B operand rows of this lane's key: K (P wave) or V (dS wave), zero past
@@ -585,6 +528,7 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
       kv[ks] = ok ? *(const frag*)(src + ks * 16 + hh * 8) : z;
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // K or V complete before any tile load is counted
   f32x16_t acc[DB];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
@@ -601,55 +545,70 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
 
   ReadLanes<D> rl;
   rl.init(lane);
-  TP st;
-  float st_l = 0.f;
-  auto stage_load = [&](int c) {
-    st.load(qb, dob, rs, c * kRows, lq, tid);
-    if (tid < 2 * kRows) {
-      const int i = c * kRows + (tid & 31);
-      if (tid < kRows) {
-        const float l = i < lq ? lseb[i] : -INFINITY;
-        st_l = l == -INFINITY ? INFINITY : l * kLog2e;
-      } else {
-        st_l = i < lq ? dlb[i] : 0.f;
-      }
+  // Stage of chunk c (32 query rows) in stage c % 4: Q and dO rows through
+  // direct buffer loads (rows past the end arrive as zeros), swizzled on the
+  // global side; wave 0 also loads the rows' lse2 (lanes 0-31) and delta
+  // (lanes 32-63), zero past the end.
+  const unsigned rsb = (unsigned)(rs * sizeof(T));
+  unsigned voff[kLPT];
+#pragma unroll
+  for (int l = 0; l < kLPT; ++l) {
+    const int p = (l * kSplitNW + wave) * 64 + lane;  // 16-byte position within the tile
+    const int r = p / kCPR, pos = p % kCPR;
+    voff[l] = (unsigned)r * rsb + (unsigned)((pos ^ bswz(r)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(size_t)smem;
+  auto issue = [&](int c) {
+    const int rows = max(0, min(kRows, lq - c * kRows));
+    const unsigned sb = lds0 + (c % kStages) * kBufB;
+    const u32x4_t rq = make_rsrc((const char*)(qb + (size_t)c * kRows * rs), (unsigned)rows * rsb);
+    const u32x4_t rd = make_rsrc((const char*)(dob + (size_t)c * kRows * rs), (unsigned)rows * rsb);
+#pragma unroll
+    for (int l = 0; l < kLPT; ++l) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (l * kSplitNW + wave) * 1024);
+      dma16(rq, voff[l], m0);
+      dma16(rd, voff[l], m0 + kTileB);
+    }
+    if (wave == 0) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + 2 * kTileB);
+      if (lane < kRows)
+        dma4(make_rsrc((const char*)(a.lse2 + wi.stat0 + c * kRows), (unsigned)rows * 4),
+             (unsigned)lane * 4, m0);
+      else
+        dma4(make_rsrc((const char*)(dlb + c * kRows), (unsigned)rows * 4),
+             (unsigned)(lane - kRows) * 4, m0);
     }
   };
-  auto stage_store_at = [&](int off) {
-    FA_LDS(char)* base = smem + off;
-    st.store(base, base + TP::kTileB, tid);
-    if (tid < 2 * kRows) *(FA_LDS(float)*)(base + 2 * TP::kTileB + tid * 4) = st_l;
+  // Start of step c: this wave's part of chunk c is in once at most chunk
+  // c + 1's loads are pending (wave 0 also issues the two statistics loads,
+  // each with half of its lanes); after the barrier every part is in, and
+  // chunk c - 2's stage (last read by the dS waves in step c - 1) takes
+  // chunk c + 2.
+  auto step_begin = [&](int c) {
+    if (c + 1 < nch) {
+      if (wave == 0) vm_wait<2 * kLPT + 2>();
+      else vm_wait<2 * kLPT>();
+    } else {
+      vm_wait<0>();
+    }
+    __syncthreads();
+    if (c + 2 < nch) issue(c + 2);
   };
 
   // The dS wave runs one chunk behind its P wave: in step c the P wave
   // handles chunk c and the dS wave finishes chunk c - 1 (with the P that
   // was handed over in step c - 1) and computes dP of chunk c, so one
-  // barrier per step orders everything.  Buffers: chunk c in stage
-  // (c - c_begin) % 3, P of chunk c in half (c - c_begin) & 1.
-  if (c_begin < nch) {
-    stage_load(c_begin);
-    stage_store_at(0);
-  }
-  __syncthreads();
-  if (c_begin + 1 < nch) stage_load(c_begin + 1);
-  // end of step c: stage chunk c + 1 at byte offset sn (that stage's last
-  // readers ran in step c - 1), barrier, start loading chunk c + 2
-  auto step_end = [&](int c, int sn) {
-    if (c + 1 < nch) stage_store_at(sn);
-    __syncthreads();
-    if (c + 2 < nch) stage_load(c + 2);
-  };
-  // byte offset of the stage after the one at byte offset sc
-  auto next_stage = [](int sc) { return sc == (kStages - 1) * kBufB ? 0 : sc + kBufB; };
+  // barrier per step orders everything.  P of chunk c sits in half c & 1.
+  if (c_begin < nch) issue(c_begin);
+  if (c_begin + 1 < nch) issue(c_begin + 1);
   // the two kinds of wave run separate loops with the same barriers
   if (pw) {
-    int sc = 0, ph = 0;  // stage (bytes) and P half (elements) of chunk c
     for (int c = c_begin; c <= nch; ++c) {
-      const int sn = next_stage(sc);
-      const FA_LDS(char)* base = smem + sc;
+      step_begin(c);
+      const FA_LDS(char)* base = smem + (c % kStages) * kBufB;
       const FA_LDS(char)* tq = base;
-      const FA_LDS(char)* tdo = base + TP::kTileB;
-      const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * TP::kTileB);
+      const FA_LDS(char)* tdo = base + kTileB;
+      const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * kTileB);
       if (wave_live && c < nch && c >= c_wave) {
         const int q0 = c * kRows;
         f32x16_t sd = {};  // S: query rows along registers
@@ -681,7 +640,7 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
             pd[r] = p[r];
           }
         }
-        FA_LDS(f32x4_t)* px = pex + ph;
+        FA_LDS(f32x4_t)* px = pex + (c & 1) * kPB;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           px[g * 64] = f32x4_t{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
@@ -701,21 +660,16 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
           for (int db = 0; db < DB; ++db)
             acc[db] = mma(tr_frag<frag>(tdo, rl.trl[db], t, RB), pk[t], acc[db]);
       }
-      step_end(c, sn);
-      sc = sn;
-      ph ^= kPB;
     }
   } else {
     f32x16_t dpp = {};  // dP of the previous chunk
-    // stages (bytes) of chunks c - 1 and c, P half (elements) of chunk c - 1
-    int sp = (kStages - 1) * kBufB, sc = 0, ph = kPB;
     for (int c = c_begin; c <= nch; ++c) {
-      const int sn = next_stage(sc);
+      step_begin(c);
       if (wave_live && c > c_begin && c - 1 >= c_wave) {
         // chunk c - 1: dS = P o (dP - delta), dK^T += Q^T dS
-        const FA_LDS(char)* bp = smem + sp;
-        const FA_LDS(float)* tlp = (const FA_LDS(float)*)(bp + 2 * TP::kTileB);
-        const FA_LDS(f32x4_t)* px = pex + ph;
+        const FA_LDS(char)* bp = smem + ((c - 1) % kStages) * kBufB;
+        const FA_LDS(float)* tlp = (const FA_LDS(float)*)(bp + 2 * kTileB);
+        const FA_LDS(f32x4_t)* px = pex + ((c - 1) & 1) * kPB;
         float ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -749,15 +703,11 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
       }
       if (wave_live && c < nch && c >= c_wave) {
         // chunk c: dP = dO V^T
-        const FA_LDS(char)* tdo = smem + sc + TP::kTileB;
+        const FA_LDS(char)* tdo = smem + (c % kStages) * kBufB + kTileB;
         dpp = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) dpp = mma(row_frag<frag>(tdo, rl.rowl[ks]), kv[ks], dpp);
       }
-      step_end(c, sn);
-      sp = sc;
-      sc = sn;
-      ph ^= kPB;
     }
   }
 
