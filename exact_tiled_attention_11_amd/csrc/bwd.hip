@@ -77,6 +77,15 @@ __device__ __forceinline__ float dot8_16(const u32x4_t& x, const u32x4_t& y) {
   return s;
 }
 
+// An LDS address held in a VGPR the compiler may not take apart: reads at a
+// constant distance from it then carry that distance in their offset field,
+// where the compiler would otherwise keep one base register per read and add
+// the ring-stage offset to each of them on every step.
+__device__ __forceinline__ const FA_LDS(char)* lds_pin(unsigned a) {
+  asm volatile("" : "+v"(a));
+  return (const FA_LDS(char)*)a;
+}
+
 // Lane parts of the two LDS read patterns of a 32-row tile.
 template <int D>
 struct ReadLanes {
@@ -94,6 +103,16 @@ struct ReadLanes {
       const int ch = 4 * i + 2 * (g & 1) + (qq >> 1);
       trl[i] = rr * RB + ((ch ^ bswz(rr)) * 16) + (qq & 1) * 8;
     }
+  }
+  // this lane's read addresses in the tile at LDS address `base` (uniform:
+  // kept whole in a scalar register, one vector add per address)
+  __device__ __forceinline__ void at(unsigned base, const FA_LDS(char)* (&rp)[KS],
+                                     const FA_LDS(char)* (&tp)[DB]) const {
+asm volatile("" : "+s"(base));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rp[ks] = lds_pin(base + rowl[ks]);
+#pragma unroll
+    for (int i = 0; i < DB; ++i) tp[i] = lds_pin(base + trl[i]);
   }
 };
 
@@ -346,25 +365,28 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
   };
 
   auto compute = [&](int c, int buf) {
-    const FA_LDS(char)* base = smem + buf * kBufB;
-    const FA_LDS(char)* tq = base;
-    const FA_LDS(char)* tdo = base + kTileB;
-    const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * kTileB);
+    // Q tile at the stage's start, dO kTileB further, lse2 and delta after both
+    unsigned sb = lds0 + buf * kBufB;
+    asm volatile("" : "+s"(sb));
+    const FA_LDS(char)* rp[KS];
+    const FA_LDS(char)* tp[DB];
+    rl.at(sb, rp, tp);
+    const FA_LDS(float)* tl = (const FA_LDS(float)*)lds_pin(sb + 2 * kTileB + 16 * hh);
     const int q0 = c * kRows;
     // S = Q K^T and dP = dO V^T: rows (queries) along registers, lanes = keys
     f32x16_t s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mma(row_frag<frag>(tq, rl.rowl[ks]), kf[ks], s);
-      dp = mma(row_frag<frag>(tdo, rl.rowl[ks]), vf[ks], dp);
+      s = mma(row_frag<frag>(rp[ks], 0), kf[ks], s);
+      dp = mma(row_frag<frag>(rp[ks], kTileB), vf[ks], dp);
     }
     // register r holds query row 8*(r>>2) + 4*hh + (r&3) of the chunk
     float lr[16], dr[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-      const f32x4_t l4 = *(const FA_LDS(f32x4_t)*)(tl + 8 * g + 4 * hh);
-      const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tl + kRows + 8 * g + 4 * hh);
+      const f32x4_t l4 = *(const FA_LDS(f32x4_t)*)(tl + 8 * g);
+      const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tl + kRows + 8 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         lr[4 * g + e] = l4[e];
@@ -408,8 +430,8 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
     for (int t = 0; t < TS; ++t)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dva[db] = mma(tr_frag<frag>(tdo, rl.trl[db], t, RB), pk[t], dva[db]);
-        dka[db] = mma(tr_frag<frag>(tq, rl.trl[db], t, RB), dk[t], dka[db]);
+        dva[db] = mma(tr_frag<frag>(tp[db], kTileB, t, RB), pk[t], dva[db]);
+        dka[db] = mma(tr_frag<frag>(tp[db], 0, t, RB), dk[t], dka[db]);
       }
   };
 
@@ -605,19 +627,21 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
   if (pw) {
     for (int c = c_begin; c <= nch; ++c) {
       step_begin(c);
-      const FA_LDS(char)* base = smem + (c % kStages) * kBufB;
-      const FA_LDS(char)* tq = base;
-      const FA_LDS(char)* tdo = base + kTileB;
-      const FA_LDS(float)* tl = (const FA_LDS(float)*)(base + 2 * kTileB);
       if (wave_live && c < nch && c >= c_wave) {
+        unsigned sb = lds0 + (c % kStages) * kBufB;
+        asm volatile("" : "+s"(sb));
+        const FA_LDS(char)* rp[KS];
+        const FA_LDS(char)* tp[DB];
+        rl.at(sb, rp, tp);
+        const FA_LDS(float)* tl = (const FA_LDS(float)*)lds_pin(sb + 2 * kTileB + 16 * hh);
         const int q0 = c * kRows;
         f32x16_t sd = {};  // S: query rows along registers
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sd = mma(row_frag<frag>(tq, rl.rowl[ks]), kv[ks], sd);
+        for (int ks = 0; ks < KS; ++ks) sd = mma(row_frag<frag>(rp[ks], 0), kv[ks], sd);
         float lr[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4_t l4 = *(const FA_LDS(f32x4_t)*)(tl + 8 * g + 4 * hh);
+          const f32x4_t l4 = *(const FA_LDS(f32x4_t)*)(tl + 8 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) lr[4 * g + e] = l4[e];
         }
@@ -658,7 +682,7 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
         for (int t = 0; t < TS; ++t)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            acc[db] = mma(tr_frag<frag>(tdo, rl.trl[db], t, RB), pk[t], acc[db]);
+            acc[db] = mma(tr_frag<frag>(tp[db], kTileB, t, RB), pk[t], acc[db]);
       }
     }
   } else {
@@ -667,14 +691,18 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
       step_begin(c);
       if (wave_live && c > c_begin && c - 1 >= c_wave) {
         // chunk c - 1: dS = P o (dP - delta), dK^T += Q^T dS
-        const FA_LDS(char)* bp = smem + ((c - 1) % kStages) * kBufB;
-        const FA_LDS(float)* tlp = (const FA_LDS(float)*)(bp + 2 * kTileB);
+        unsigned sb = lds0 + ((c - 1) % kStages) * kBufB;
+        asm volatile("" : "+s"(sb));
+        const FA_LDS(char)* tp[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) tp[db] = lds_pin(sb + rl.trl[db]);
+        const FA_LDS(float)* tlp = (const FA_LDS(float)*)lds_pin(sb + 2 * kTileB + 16 * hh);
         const FA_LDS(f32x4_t)* px = pex + ((c - 1) & 1) * kPB;
         float ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4_t p4 = px[g * 64];
-          const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tlp + kRows + 8 * g + 4 * hh);
+          const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tlp + kRows + 8 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
@@ -699,14 +727,16 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
         for (int t = 0; t < TS; ++t)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            acc[db] = mma(tr_frag<frag>(bp, rl.trl[db], t, RB), pk[t], acc[db]);
+            acc[db] = mma(tr_frag<frag>(tp[db], 0, t, RB), pk[t], acc[db]);
       }
       if (wave_live && c < nch && c >= c_wave) {
         // chunk c: dP = dO V^T
-        const FA_LDS(char)* tdo = smem + (c % kStages) * kBufB + kTileB;
+        unsigned sb = lds0 + (c % kStages) * kBufB + kTileB;
+        asm volatile("" : "+s"(sb));
         dpp = f32x16_t{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dpp = mma(row_frag<frag>(tdo, rl.rowl[ks]), kv[ks], dpp);
+        for (int ks = 0; ks < KS; ++ks)
+          dpp = mma(row_frag<frag>(lds_pin(sb + rl.rowl[ks]), 0), kv[ks], dpp);
       }
     }
   }
@@ -830,15 +860,17 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
     }
   };
   auto compute = [&](int j, int buf) {
-    const FA_LDS(char)* tk = smem + buf * kBufB;
-    const FA_LDS(char)* tv = tk + kTileB;
+    // K tile at the stage's start, V kTileB further
+    const FA_LDS(char)* rp[KS];
+    const FA_LDS(char)* tp[DB];
+    rl.at(lds0 + buf * kBufB, rp, tp);
     const int k0 = j * kRows;
     // S^T = K Q^T and dP^T = V dO^T: keys along registers, lanes = queries
     f32x16_t s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mma(row_frag<frag>(tk, rl.rowl[ks]), qf[ks], s);
-      dp = mma(row_frag<frag>(tv, rl.rowl[ks]), dof[ks], dp);
+      s = mma(row_frag<frag>(rp[ks], 0), qf[ks], s);
+      dp = mma(row_frag<frag>(rp[ks], kTileB), dof[ks], dp);
     }
     const bool masked = (k0 + kRows > lk) || (CAUSAL && k0 + kRows - 1 > max(wq0 + off, pre));
     // key 8*(r>>2) + 4*hh + (r&3) of the block is visible iff that offset <= lim
@@ -895,7 +927,7 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
 #pragma unroll
     for (int t = 0; t < TS; ++t)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dqa[db] = mma(tr_frag<frag>(tk, rl.trl[db], t, RB), dsk[t], dqa[db]);
+      for (int db = 0; db < DB; ++db) dqa[db] = mma(tr_frag<frag>(tp[db], 0, t, RB), dsk[t], dqa[db]);
     if constexpr (kPrio) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
