@@ -176,8 +176,9 @@ __device__ __forceinline__ BwdItem bwd_item(const BwdArgs& a) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// delta = rowsum(dO o O) and lse2 = lse * log2 e for every (query row, head),
-// in lse's layout
+// -delta = -rowsum(dO o O) and lse2 = lse * log2 e for every (query row,
+// head), in lse's layout (stored negated: the dK/dV kernels start their dP
+// products from it, so dP - delta comes out of the matrix cores)
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
     const int b = (int)(tok / a.Nq);
     idx = ((long long)b * a.H + h) * a.Nq + i;
   }
-  a.delta[idx] = s;
+  a.delta[idx] = -s;
   // the row's exp2 offset for the gradient kernels: probabilities are
   // exp2(c s - lse2); +inf for a row with no visible key (probability 0)
   const float l = a.lse[idx];
@@ -374,14 +375,11 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
     const FA_LDS(float)* tl = (const FA_LDS(float)*)lds_pin(sb + 2 * kTileB + 16 * hh);
     const int q0 = c * kRows;
     // S = Q K^T and dP = dO V^T: rows (queries) along registers, lanes = keys
-    f32x16_t s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mma(row_frag<frag>(rp[ks], 0), kf[ks], s);
-      dp = mma(row_frag<frag>(rp[ks], kTileB), vf[ks], dp);
-    }
-    // register r holds query row 8*(r>>2) + 4*hh + (r&3) of the chunk
-    float lr[16], dr[16];
+    // register r holds query row 8*(r>>2) + 4*hh + (r&3) of the chunk; nd:
+    // -delta of those rows, where the dP products start (without dropout,
+    // whose dS scales dP first)
+    float lr[16];
+    f32x16_t nd;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -390,8 +388,14 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         lr[4 * g + e] = l4[e];
-        dr[4 * g + e] = d4[e];
+        nd[4 * g + e] = d4[e];
       }
+    }
+    f32x16_t s = {}, dp = DROP ? f32x16_t{} : nd;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mma(row_frag<frag>(rp[ks], 0), kf[ks], s);
+      dp = mma(row_frag<frag>(rp[ks], kTileB), vf[ks], dp);
     }
     const bool masked =
         (kw0 + kRows - 1 >= lk) || (CAUSAL && kw0 + kRows - 1 > max(q0 + off, pre));
@@ -407,10 +411,10 @@ __global__ __launch_bounds__(kNW * 64, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Bwd
       if constexpr (DROP) {
         const bool kp = kept(kw[r >> 2], r & 3, a.drop_t);
         pd[r] = kp ? p[r] : 0.f;
-        ds[r] = p[r] * ((kp ? dp[r] * a.drop_scale : 0.f) - dr[r]);
+        ds[r] = p[r] * ((kp ? dp[r] * a.drop_scale : 0.f) + nd[r]);
       } else {
         pd[r] = p[r];
-        ds[r] = p[r] * (dp[r] - dr[r]);
+        ds[r] = p[r] * dp[r];  // dp holds dP - delta
       }
     }
     frag pk[TS], dk[TS];
@@ -690,7 +694,8 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
     for (int c = c_begin; c <= nch; ++c) {
       step_begin(c);
       if (wave_live && c > c_begin && c - 1 >= c_wave) {
-        // chunk c - 1: dS = P o (dP - delta), dK^T += Q^T dS
+        // chunk c - 1: dS = P o (dP - delta), dK^T += Q^T dS (without
+        // dropout dpp already holds dP - delta)
         unsigned sb = lds0 + ((c - 1) % kStages) * kBufB;
         asm volatile("" : "+s"(sb));
         const FA_LDS(char)* tp[DB];
@@ -702,15 +707,15 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x4_t p4 = px[g * 64];
-          const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tlp + kRows + 8 * g);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             if constexpr (DROP) {
+              const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tlp + kRows + 8 * g);
               const bool kp = !__builtin_signbit(p4[e]);
-              ds[r] = fabsf(p4[e]) * ((kp ? dpp[r] * a.drop_scale : 0.f) - d4[e]);
+              ds[r] = fabsf(p4[e]) * ((kp ? dpp[r] * a.drop_scale : 0.f) + d4[e]);
             } else {
-              ds[r] = p4[e] * (dpp[r] - d4[e]);
+              ds[r] = p4[e] * dpp[r];
             }
           }
         }
@@ -730,10 +735,21 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
             acc[db] = mma(tr_frag<frag>(tp[db], 0, t, RB), pk[t], acc[db]);
       }
       if (wave_live && c < nch && c >= c_wave) {
-        // chunk c: dP = dO V^T
+        // chunk c: dP = dO V^T (without dropout: -delta + dO V^T, the
+        // products starting from the rows' -delta)
         unsigned sb = lds0 + (c % kStages) * kBufB + kTileB;
         asm volatile("" : "+s"(sb));
-        dpp = f32x16_t{};
+        if constexpr (DROP) {
+          dpp = f32x16_t{};
+        } else {
+          const FA_LDS(float)* tln = (const FA_LDS(float)*)lds_pin(sb + kTileB + 16 * hh);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t d4 = *(const FA_LDS(f32x4_t)*)(tln + kRows + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dpp[4 * g + e] = d4[e];
+          }
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           dpp = mma(row_frag<frag>(lds_pin(sb + rl.rowl[ks]), 0), kv[ks], dpp);
@@ -800,7 +816,7 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
 
   // Q and dO rows of this lane's query (B operands), lse and delta
   frag qf[KS], dof[KS];
-  float lrow = INFINITY, drow = 0.f;
+  float lrow = INFINITY, ndrow = 0.f;  // lse2 and -delta of this lane's row
   {
     const bool ok = qi < lq;
     const size_t ro = ((size_t)wi.q_tok0 + (ok ? qi : 0)) * rs + (size_t)h * D;
@@ -812,7 +828,7 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
     }
     if (ok) {
       lrow = a.lse2[wi.stat0 + qi];
-      drow = a.delta[wi.stat0 + qi];
+      ndrow = a.delta[wi.stat0 + qi];
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // Q, dO and the row statistics complete before any tile load
@@ -907,9 +923,9 @@ __global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) 
           const int r = 8 * t + 2 * e + z;
           const float p = fast_exp2(x[r]);
           if constexpr (DROP)
-            pr[z] = p * ((kept(kw[r >> 2], r & 3, a.drop_t) ? dp[r] * a.drop_scale : 0.f) - drow);
+            pr[z] = p * ((kept(kw[r >> 2], r & 3, a.drop_t) ? dp[r] * a.drop_scale : 0.f) + ndrow);
           else
-            pr[z] = p * (dp[r] - drow);
+            pr[z] = p * (dp[r] + ndrow);
         }
         ud[e] = pack2(pr[0], pr[1], (T*)nullptr);
       }

@@ -91,7 +91,7 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;        // [B, H, Nq]
-  float* delta;            // workspace [B, H, Nq]: rowsum(dO * O)
+  float* delta;            // workspace [B, H, Nq]: -rowsum(dO * O)
   float* lse2;             // workspace, delta's layout: lse * log2 e (+inf: no visible key)
   void* dq;
   void* dk;
