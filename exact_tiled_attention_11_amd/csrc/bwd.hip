@@ -785,10 +785,10 @@ __global__ __launch_bounds__(kSplitNW * 64, 1) void bwd_dkdv_split_kernel(BwdArg
 // ---------------------------------------------------------------------------
 // dQ: a workgroup per 128 query rows of one (batch, head)
 // ---------------------------------------------------------------------------
-// (four waves per SIMD fit the causal head_dim-64 instance without spills,
-// measured 1 % faster; the others keep the compiler's choice)
+// (four waves per SIMD fit the causal head_dim-64 instances without dropout
+// with no spills, measured 1 % faster; the others keep the compiler's choice)
 template <typename T, int D, bool CAUSAL, int MODE, bool VARLEN>
-__global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && MODE == kBwdPlain) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kNW * 64, (D == 64 && CAUSAL && (MODE & kBwdDrop) == 0) ? 4 : 2) void bwd_dq_kernel(BwdArgs a) {
   constexpr bool DROP = (MODE & kBwdDrop) != 0, ALIBI = (MODE & kBwdAlibi) != 0;
   using E = Elem<T>;
   using frag = typename E::frag;
