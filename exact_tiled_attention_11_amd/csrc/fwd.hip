@@ -649,8 +649,13 @@ using IC = std::integral_constant<int, N>;
 // place in the dropout counters); the prefix mask is a runtime value in all.
 constexpr int kPipePlain = 0, kPipeAlibi = 1, kPipeDrop = 2;
 
+// Waves per SIMD: four at head_dim 64 (128 VGPRs), three for the ALiBi
+// instances (their score bias vector takes 16 more), two at head_dim 128.
+template <int D, int MODE>
+constexpr int pipe_occupancy() { return D == 64 ? ((MODE & 1) ? 3 : 4) : 2; }
+
 template <typename T, int D, int NW, int PK, bool CAUSAL, bool VARLEN, int MODE>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe_kernel(FwdArgs a) {
   constexpr bool ALIBI = (MODE & kPipeAlibi) != 0;
   constexpr bool DROP = (MODE & kPipeDrop) != 0;
   using C = PipeCfg<T, D, NW, PK>;
@@ -682,6 +687,15 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   const int lq = wi.lq, lk = wi.lk;
   float slope2 = 0.f;  // ALiBi slope of this head, in exp2 units
   if constexpr (ALIBI) slope2 = a.alibi[wi.h] * kLog2e;
+  // ALiBi: the score MFMAs of every block start from slope2 * (8*(r>>2) +
+  // (r&3)) / c in register r, the per-register part of the bias (the keys of
+  // a block in the registers' order, less the lane half's 4*hh), so that
+  // c * s carries it and no score needs an operation of its own for it
+  f32x16_t sinit = {};
+  if constexpr (ALIBI) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sinit[r] = slope2 * (float)(8 * (r >> 2) + (r & 3)) / a.c;
+  }
 
   const int q0 = wi.qblk * C::kBR;
   const int off = lk - lq;  // bottom-right causal alignment
@@ -828,7 +842,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
   // S^T = K Q^T of block 0 into sS
   auto scores0 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sS = mma(kfrag(IC<0>{}, ks), qf[ks], ks == 0 ? f32x16_t{} : sS);
+    for (int ks = 0; ks < KS; ++ks) sS = mma(kfrag(IC<0>{}, ks), qf[ks], ks == 0 ? sinit : sS);
   };
   // Dropout: keep words of the current block (word g: registers 4g..4g+3).
   // The row sums take every probability; the P V operand only the kept ones
@@ -925,8 +939,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     // (r&3) of the block, position qi + off.  In a causal block left of the
     // wave's first row every key is at or before the position, so the bias is
     // slope * (key - position): a per-lane part joins the exponent's addend
-    // and the per-element part slope * (8*(r>>2) + (r&3)) is one FMA with a
-    // literal.  Other blocks take the absolute value (two operations).
+    // and the per-element part slope * (8*(r>>2) + (r&3)) came with the
+    // scores (sinit).  Other blocks take that part back out with the
+    // absolute value (two operations per score).
     bool lin = false;
     float dbase = 0.f;
     if constexpr (ALIBI) {
@@ -937,15 +952,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
 #pragma unroll
     for (int r = 0; r < 16; ++r) sX[r] = __builtin_fmaf(sS[r], a.c, addend);
     if constexpr (ALIBI) {
-      if (lin) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sX[r] = __builtin_fmaf(slope2, (float)(8 * (r >> 2) + (r & 3)), sX[r]);
-      } else {
+      if (!lin) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float d = dbase + (float)(8 * (r >> 2) + (r & 3));
-          sX[r] = __builtin_fmaf(-slope2, fabsf(d), sX[r]);
+          const float e = (float)(8 * (r >> 2) + (r & 3));
+          sX[r] = __builtin_fmaf(-slope2, fabsf(dbase + e) + e, sX[r]);
         }
       }
     }
@@ -956,7 +967,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 4 : 2) void fwd_pipe_kernel(FwdA
     };
     auto mf = [&](int i) __attribute__((always_inline)) {
       if (i < NPV) oacc[i % DB] = mma(op[i], pk[i / DB], oacc[i % DB]);
-      else sS = mma(op[i], qf[i - NPV], i == NPV ? f32x16_t{} : sS);
+      else sS = mma(op[i], qf[i - NPV], i == NPV ? sinit : sS);
     };
     float pe[16];
     auto exp2c = [&](int c) __attribute__((always_inline)) {
@@ -1273,7 +1284,8 @@ hipError_t launch_fwd(const FwdArgs& args, fa_dtype_t dtype, int D, bool causal,
                       unsigned grid, hipStream_t stream) {
   FwdArgs a = args;
   // the head_dim-64 pipelined kernel runs four workgroups per compute unit
-  a.tail_prio = dtype != FA_F32 && D == 64 && (long long)grid <= 4LL * cu_count();
+  // (three with ALiBi): a grid of at most that many is one round
+  a.tail_prio = dtype != FA_F32 && D == 64 && (long long)grid <= (a.alibi ? 3LL : 4LL) * cu_count();
   switch (dtype) {
     case FA_BF16:
       return D == 64 ? launch_t<__bf16, 64>(a, causal, varlen, grid, stream)
