@@ -780,7 +780,20 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
   float mrow = -INFINITY;  // running offset (units of scale*log2 e); -inf: no key yet
   float lrow = 0.f;        // running sum over this lane's keys
   float negm = 0.f;        // -mrow, 0 while the row has seen no key
-  float thr = -1.f;        // a block sum above this settles: 2^15, or -1 while fresh
+  // A block sum above thr settles (-1 while the row is fresh).  The bound
+  // keeps every probability representable in the P V operand: 2^15 for fp16
+  // (largest finite 65504); bf16 has fp32's exponent range, so 2^60 there,
+  // which lets a row's offset lag further behind a growing maximum (ALiBi's
+  // bias rises by slope * 32 per block) before the block has to be redone.
+  constexpr float kThr = __is_same(T, __bf16) ? 0x1p60f : 0x1p15f;
+  // With ALiBi in bf16 a settle also places the offset kLead above the block
+  // maximum: the block's probabilities are then at most 2^-48 (far inside
+  // bf16's and fp32's range; the offset cancels in O / l and lse), and the
+  // growth that a bias rising block by block brings is absorbed for
+  // kLead + 60 units instead of 60.  Not with fp16, whose P operand would
+  // lose such small values.
+  constexpr float kLead = (ALIBI && __is_same(T, __bf16)) ? 48.f : 0.f;
+  float thr = -1.f;
   __syncthreads();         // LDS zeroed before any block lands
 
   int klane[KS];
@@ -874,8 +887,8 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
     }
     return ts;
   };
-  // lazy offset: raise m only if a probability could exceed 2^15 or the row
-  // has seen no key yet; then rescale O and l and redo the block
+  // lazy offset: raise m only if a probability could exceed the bound above
+  // or the row has seen no key yet; then rescale O and l and redo the block
   auto settle = [&](float ts) __attribute__((always_inline)) {
     // thr is -1 while the row has seen no key, so one compare covers both cases
     const uint64_t need = __builtin_amdgcn_ballot_w64(!(ts <= thr));
@@ -887,13 +900,13 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
       const bool fresh = mrow == -INFINITY;
       const bool none = !(mx > -1e30f);  // no visible key in this block
       float delta;
-      if (fresh) delta = none ? 0.f : mx;
-      else delta = mx > kTau ? mx : 0.f;
+      if (fresh) delta = none ? 0.f : mx + kLead;
+      else delta = mx > kTau ? mx + kLead : 0.f;
       const float mold = fresh ? 0.f : mrow;
       const float alpha = fresh ? 0.f : fast_exp2(-delta);
       mrow = (fresh && none) ? -INFINITY : mold + delta;
       negm = (fresh && none) ? 0.f : -mrow;
-      thr = (fresh && none) ? -1.f : 0x1p15f;
+      thr = (fresh && none) ? -1.f : kThr;
       lrow *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
