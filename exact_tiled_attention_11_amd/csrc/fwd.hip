@@ -998,7 +998,12 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
       float p0 = pe[2 * c], p1 = pe[2 * c + 1];
       drop2(c, p0, p1);
       u32x4_t w = __builtin_bit_cast(u32x4_t, pk[c >> 2]);
-      w[c & 3] = pack2(p0, p1, (T*)nullptr);
+      unsigned pw = pack2(p0, p1, (T*)nullptr);
+      // held here: left free, the compiler sinks the packs below the settle
+      // test, which keeps the 16 unrounded probabilities live across it (7
+      // more VGPRs, and spills in the dropout instance)
+      asm volatile("" : "+v"(pw));
+      w[c & 3] = pw;
       pk[c >> 2] = __builtin_bit_cast(frag, w);
     };
     // pair p: exp2 in chunk p*RP, add and pack in chunk p*RP + ALAG; the
