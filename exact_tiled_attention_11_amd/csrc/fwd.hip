@@ -235,6 +235,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 
   // zero LDS once so no stale bit pattern can ever enter P V
   for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
+  __syncthreads();  // LDS zeroed before any tile lands
+  // the first tiles are requested before Q is read, so that their memory
+  // latency and Q's overlap
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nkt) issue(p);
 
   // ---- Q block of this wave, held as MFMA B operands ----
   frag qf[QB][KS];
@@ -253,9 +259,9 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       }
     }
   }
-  // Q must be complete before the loop: its loads are the only vector-memory
-  // reads the compiler tracks, and a pending one would make it wait for all
-  // tile loads in flight at the first use inside the loop.
+  // Q (and the first tiles) must be complete before the loop: Q's loads are
+  // the only vector-memory reads the compiler tracks, and a pending one would
+  // make it wait for all tile loads in flight at the first use inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
 
   f32x16_t oacc[DB][QB];
@@ -267,11 +273,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db][qb] = f32x16_t{};
   }
-  __syncthreads();  // LDS zeroed before any tile lands
-
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nkt) issue(p);
 
   // Lane parts of the LDS read addresses (byte offsets within a tile).  The
   // swizzle term of a row depends only on the row's low bits, which these
@@ -475,11 +476,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       }
     }
   };
-
-
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nkt) issue(p);
 
   for (int j = 0; j < nkt; ++j) {
     // tile j has landed once at most the loads of the later tiles already
@@ -761,18 +757,7 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
 
   for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
 
-  frag qf[KS];
-  {
-    const int qi = wq0 + col;
-    const bool ok = qi < lq;
-    const T* row = qp + (size_t)(ok ? qi : 0) * rs;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      frag z = {};
-      qf[ks] = ok ? *(const frag*)(row + ks * 16 + hh * 8) : z;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // Q complete before any block load is counted
+  frag qf[KS];  // Q rows of this wave (B operands), read after the first block requests
 
   f32x16_t oacc[DB];
 #pragma unroll
@@ -1068,9 +1053,21 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
   [&]<int... S>(std::integer_sequence<int, S...>) {
     (issue(S - PK - 1, IC<(S - PK - 1 + 4 * C::kNS) % C::kNS>{}), ...);
   }(std::make_integer_sequence<int, PK + 1>{});
-  if constexpr (!C::kSplitKV) vm_wait<(2 * PK + 1) * LPS>();  // K of block 0 is in
-  else if (loads_k) vm_wait<PK * LPS>();
-  __syncthreads();
+  // Q is read while those requests are in flight (the two memory latencies
+  // overlap); it must be complete before any block load is counted: its loads
+  // are the only vector-memory reads the compiler tracks
+  {
+    const int qi = wq0 + col;
+    const bool ok = qi < lq;
+    const T* row = qp + (size_t)(ok ? qi : 0) * rs;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      qf[ks] = ok ? *(const frag*)(row + ks * 16 + hh * 8) : z;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // Q and the first blocks are in
+  __syncthreads();                // every wave's part of them too
   if (nw > 0) scores0();
   // steps 0 .. nst, unrolled by kNS so every slot offset is a constant (the
   // steps past nst issue empty requests and compute nothing)
