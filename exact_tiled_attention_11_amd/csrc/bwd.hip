@@ -306,20 +306,9 @@ __global__ __launch_bounds__(kNW * 64, (dkdv_occupancy<D, MODE>())) void bwd_dkd
   const T* dob = (const T*)a.dout + (size_t)wi.q_tok0 * rs + (size_t)h * D;
   const float* dlb = a.delta + wi.stat0;
 
-  // K and V rows of this lane's key (B operands), zero past the real keys
+  // K and V rows of this lane's key (B operands, zero past the real keys),
+  // read after the first chunk requests
   frag kf[KS], vf[KS];
-  {
-    const bool ok = n < lk;
-    const T* kr = (const T*)a.k + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs + (size_t)h * D;
-    const T* vr = (const T*)a.v + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs + (size_t)h * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      frag z = {};
-      kf[ks] = ok ? *(const frag*)(kr + ks * 16 + hh * 8) : z;
-      vf[ks] = ok ? *(const frag*)(vr + ks * 16 + hh * 8) : z;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // K and V complete before any tile load is counted
   f32x16_t dka[DB], dva[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dka[db] = dva[db] = f32x16_t{};
@@ -451,6 +440,20 @@ __global__ __launch_bounds__(kNW * 64, (dkdv_occupancy<D, MODE>())) void bwd_dkd
 
   if (c_begin < nch) issue(c_begin);
   if (c_begin + 1 < nch) issue(c_begin + 1);
+  // K and V are read while those requests are in flight (the two memory
+  // latencies overlap); complete before any chunk load is counted
+  {
+    const bool ok = n < lk;
+    const T* kr = (const T*)a.k + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs + (size_t)h * D;
+    const T* vr = (const T*)a.v + ((size_t)wi.k_tok0 + (ok ? n : 0)) * rs + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      kf[ks] = ok ? *(const frag*)(kr + ks * 16 + hh * 8) : z;
+      vf[ks] = ok ? *(const frag*)(vr + ks * 16 + hh * 8) : z;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   for (int c = c_begin; c < nch; ++c) {
     // this wave's part of chunk c is in once at most the next chunk's loads
     // are pending (wave 0 also issues the two statistics loads, each with
@@ -1050,24 +1053,10 @@ __global__ __launch_bounds__(kNW * 64, 3) void bwd_dq_pipe_kernel(BwdArgs a) {
 
   for (int i = tid; i < 2 * kNS * kTileB / 16; i += kNW * 64) ((u32x4_t*)smem_raw)[i] = u32x4_t{};
 
-  // Q and dO rows of this lane's query (B operands), lse2 and -delta
+  // Q and dO rows of this lane's query (B operands), lse2 and -delta: read
+  // after the first block requests
   frag qf[KS], dof[KS];
   float lrow = INFINITY, ndrow = 0.f;
-  {
-    const bool ok = qi < lq;
-    const size_t ro = ((size_t)wi.q_tok0 + (ok ? qi : 0)) * rs + (size_t)h * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      frag z = {};
-      qf[ks] = ok ? *(const frag*)((const T*)a.q + ro + ks * 16 + hh * 8) : z;
-      dof[ks] = ok ? *(const frag*)((const T*)a.dout + ro + ks * 16 + hh * 8) : z;
-    }
-    if (ok) {
-      lrow = a.lse2[wi.stat0 + qi];
-      ndrow = a.delta[wi.stat0 + qi];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // Q, dO and the row statistics complete before any block load
   f32x16_t dqa[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = f32x16_t{};
@@ -1225,8 +1214,24 @@ __global__ __launch_bounds__(kNW * 64, 3) void bwd_dq_pipe_kernel(BwdArgs a) {
   [&]<int... S>(std::integer_sequence<int, S...>) {
     (issue(S, IC<S % kNS>{}), ...);
   }(std::make_integer_sequence<int, PK + 1>{});
-  vm_wait<2 * PK * kLPT>();  // block 0 is in
-  __syncthreads();
+  // Q, dO and the row statistics are read while those requests are in flight
+  // (the two memory latencies overlap)
+  {
+    const bool ok = qi < lq;
+    const size_t ro = ((size_t)wi.q_tok0 + (ok ? qi : 0)) * rs + (size_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      frag z = {};
+      qf[ks] = ok ? *(const frag*)((const T*)a.q + ro + ks * 16 + hh * 8) : z;
+      dof[ks] = ok ? *(const frag*)((const T*)a.dout + ro + ks * 16 + hh * 8) : z;
+    }
+    if (ok) {
+      lrow = a.lse2[wi.stat0 + qi];
+      ndrow = a.delta[wi.stat0 + qi];
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // they and the first blocks are in
+  __syncthreads();                // every wave's part of the blocks too
   if (nkw > 0) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
