@@ -102,6 +102,15 @@ BWD = [
     (P("bf16 D64 causal B5 H8 N300 (pair groups 4+1)", "bf16", 64, True, 5, 8, 300, 300, 60), None),
     (P("f16 D128 causal B3 H16 N200 (pair groups 4+2)", "f16", 128, True, 3, 16, 200, 200, 155),
      None),
+    # head_dim 64 runs the pipelined dQ kernel: its first and last steps at the edges of the key
+    # range (one key; one query row against 32 key blocks; fewer keys than one block; a long query
+    # range against two key blocks)
+    (P("bf16 D64 noncausal B1 H1 Nq1 Nk1", "bf16", 64, False, 1, 1, 1, 1, 61), None),
+    (P("bf16 D64 causal B1 H2 Nq1 Nk1000 (one query row)", "bf16", 64, True, 1, 2, 1, 1000, 62),
+     None),
+    (P("f16 D64 noncausal B1 H1 Nq40 Nk20 (keys short of one block)", "f16", 64, False, 1, 1, 40,
+       20, 63), None),
+    (P("bf16 D64 causal B1 H2 Nq2000 Nk33", "bf16", 64, True, 1, 2, 2000, 33, 64), None),
 ]
 
 
