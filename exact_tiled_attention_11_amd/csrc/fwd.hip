@@ -233,9 +233,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  // zero LDS once so no stale bit pattern can ever enter P V
-  for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
-  __syncthreads();  // LDS zeroed before any tile lands
   // the first tiles are requested before Q is read, so that their memory
   // latency and Q's overlap
 #pragma unroll
@@ -755,8 +752,6 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
     if (loads_v) load(vp, voffv, s + PK, vslot(r + PK));
   };
 
-  for (int i = tid; i < C::kLdsB / 16; i += C::kNT) smem[i] = u32x4_t{};
-
   frag qf[KS];  // Q rows of this wave (B operands), read after the first block requests
 
   f32x16_t oacc[DB];
@@ -779,7 +774,6 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
   // lose such small values.
   constexpr float kLead = (ALIBI && __is_same(T, __bf16)) ? 48.f : 0.f;
   float thr = -1.f;
-  __syncthreads();         // LDS zeroed before any block lands
 
   int klane[KS];
 #pragma unroll
