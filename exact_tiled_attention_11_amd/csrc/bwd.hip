@@ -410,6 +410,9 @@ __global__ __launch_bounds__(kNW * 64, (dkdv_occupancy<D, MODE>())) void bwd_dkd
       if constexpr (DROP) {
         const bool kp = kept(kw[r >> 2], r & 3, a.drop_t);
         pd[r] = kp ? p[r] : 0.f;
+        // (held: left free, the compiler converts each kept probability alone
+        // and merges the halves with v_perm)
+        asm volatile("" : "+v"(pd[r]));
         ds[r] = p[r] * ((kp ? dp[r] * a.drop_scale : 0.f) + nd[r]);
       } else {
         pd[r] = p[r];

@@ -976,6 +976,9 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
       }
       float p0 = pe[2 * c], p1 = pe[2 * c + 1];
       drop2(c, p0, p1);
+      // (held: left free, the compiler converts each probability alone and
+      // merges the dropped halves with v_perm, 16 more instructions a block)
+      if constexpr (DROP) asm volatile("" : "+v"(p0), "+v"(p1));
       u32x4_t w = __builtin_bit_cast(u32x4_t, pk[c >> 2]);
       unsigned pw = pack2(p0, p1, (T*)nullptr);
       // held here: left free, the compiler sinks the packs below the settle
