@@ -905,7 +905,7 @@ __global__ __launch_bounds__(NW * 64, (pipe_occupancy<D, MODE>())) void fwd_pipe
   // copies of it would not fit the register budget.
   auto step_block = [&](int u, bool masked, auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
-    if constexpr (DROP) keep_words_rows(kw, 2 * u, hh, wq0 + col, wi.h, wi.b, a.seed_lo, a.seed_hi);
+    if constexpr (DROP) keep_words_rows<D == 64 && !ALIBI>(kw, 2 * u, hh, wq0 + col, wi.h, wi.b, a.seed_lo, a.seed_hi);
     // The mask, on the raw scores: a hidden one becomes -inf (exp2 gives 0 and
     // it never wins a maximum).  Key 8*(e>>2) + 4*hh + (e&3) of the block is
     // visible to query qi iff 8*(e>>2) + (e&3) <= lim.  Written in place: a
